@@ -1,0 +1,280 @@
+"""Python binding of libspecverify (argument marshalling only).
+
+Every step of the verify path runs in the HIP kernels of libspecverify.so,
+built in-tree by ``adaptive_draft_verification_amd/build.py``.  PyTorch supplies
+device memory and streams; nothing here computes.  Importing this module
+fails loudly if the library has not been built: there is no fallback.
+
+The functions keep the C names (sv_budget_select, sv_pack_varlen, sv_verify,
+...) and take torch tensors; shapes are read from the tensors, the stream is
+torch's current stream unless one is given.  A non-OK status raises SvError.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_VALUE, SV_ERR_WORKSPACE, SV_ERR_LAUNCH = range(7)
+SV_F32, SV_BF16 = 0, 1
+SV_STOCHASTIC, SV_GREEDY = 0, 1
+SV_DEV_BAD_CU_ROWS, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE = 1, 2, 4
+SV_DEV_BAD_DRAFT_LEN, SV_DEV_BAD_COST, SV_DEV_BAD_KEPT = 8, 16, 32
+SV_MAX_BUDGET_SLOTS, SV_MAX_DRAFT, SV_MAX_VOCAB = 8192, 64, 1048576
+
+EXPORTED = ["sv_status_str", "sv_budget_workspace_bytes", "sv_verify_workspace_bytes",
+            "sv_cost_table_prepare", "sv_budget_select", "sv_pack_varlen", "sv_verify",
+            "sv_verify_stages", "sv_philox_uniforms"]
+
+
+class SvError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_lib.sv_status_str(status).decode()} (status {status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python adaptive_draft_verification_amd/build.py` "
+                          "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t)
+    sig = {
+        "sv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "sv_budget_workspace_bytes": (sz, [i32, i32]),
+        "sv_verify_workspace_bytes": (sz, [i32, i32]),
+        "sv_cost_table_prepare": (ctypes.c_int, [vp, i32, i32, vp, i32]),
+        "sv_budget_select": (ctypes.c_int, [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp,
+                                            vp, sz, vp]),
+        "sv_pack_varlen": (ctypes.c_int, [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "sv_verify": (ctypes.c_int, [vp, i64, i64, vp, i64, ctypes.c_int, i32, vp, vp, i32, i32,
+                                     ctypes.c_int, f32, u64, u64, vp, vp, vp, vp, vp, vp, vp, sz,
+                                     vp]),
+        "sv_verify_stages": (ctypes.c_int, [vp, i64, i64, vp, i64, ctypes.c_int, i32, vp, vp, i32,
+                                            i32, ctypes.c_int, f32, u64, u64, vp, vp, vp, vp, vp,
+                                            vp, vp, sz, i32, vp]),
+        "sv_philox_uniforms": (ctypes.c_int, [u64, u64, i32, i32, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name, ndim=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def _check(status, where):
+    if status != SV_OK:
+        raise SvError(status, where)
+
+
+def sv_status_str(status):
+    return _lib.sv_status_str(status).decode()
+
+
+def sv_budget_workspace_bytes(n_req, k_max):
+    return int(_lib.sv_budget_workspace_bytes(n_req, k_max))
+
+
+def sv_verify_workspace_bytes(n_req, k_max):
+    return int(_lib.sv_verify_workspace_bytes(n_req, k_max))
+
+
+def sv_cost_table_prepare(raw, granule, out_len):
+    """Host call: shaped cost table (numpy fp32 in, numpy fp32 out)."""
+    raw = np.ascontiguousarray(raw, dtype=np.float32)
+    out = np.zeros(int(out_len), dtype=np.float32)
+    _check(_lib.sv_cost_table_prepare(raw.ctypes.data_as(ctypes.c_void_p), len(raw), int(granule),
+                                      out.ctypes.data_as(ctypes.c_void_p), int(out_len)),
+           "sv_cost_table_prepare")
+    return out
+
+
+def sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survival=None,
+                     dev_error=None, stream=None):
+    """conf [n, k_max] f32, draft_len [n] i32, cost [L] f32 -> kept [n] i32, budget [1] i32."""
+    _dev(conf, torch.float32, "conf", 2)
+    _dev(draft_len, torch.int32, "draft_len", 1)
+    _dev(cost, torch.float32, "cost", 1)
+    _dev(kept, torch.int32, "kept", 1)
+    _dev(budget, torch.int32, "budget", 1)
+    _dev(survival, torch.float32, "survival", 2)
+    _dev(dev_error, torch.int32, "dev_error", 1)
+    n, k_max = conf.shape
+    if draft_len.numel() != n or kept.numel() != n or budget.numel() < 1:
+        raise ValueError("draft_len, kept must have n entries and budget one")
+    if survival is not None and tuple(survival.shape) != (n, k_max):
+        raise ValueError("survival must be [n, k_max]")
+    _check(_lib.sv_budget_select(_ptr(conf), _ptr(draft_len), n, k_max, _ptr(cost), cost.numel(),
+                                 int(t_base), int(n_bonus), _ptr(kept), _ptr(budget),
+                                 _ptr(survival), _ptr(dev_error), None, 0, _stream(stream)),
+           "sv_budget_select")
+
+
+def sv_pack_varlen(kept, last_token, draft_tokens, cu_rows, row_req, row_pos, packed_tokens,
+                   dev_error=None, stream=None):
+    """kept [n], last_token [n], draft_tokens [n, k_max] -> cu_rows [n+1], row maps [n(k_max+1)]."""
+    for name, t in (("kept", kept), ("last_token", last_token), ("cu_rows", cu_rows),
+                    ("row_req", row_req), ("row_pos", row_pos), ("packed_tokens", packed_tokens)):
+        _dev(t, torch.int32, name, 1)
+    _dev(draft_tokens, torch.int32, "draft_tokens", 2)
+    _dev(dev_error, torch.int32, "dev_error", 1)
+    n, k_max = draft_tokens.shape
+    cap = n * (k_max + 1)
+    if kept.numel() != n or last_token.numel() != n or cu_rows.numel() != n + 1:
+        raise ValueError("kept/last_token need n entries, cu_rows n+1")
+    if row_req.numel() != cap or row_pos.numel() != cap or packed_tokens.numel() != cap:
+        raise ValueError("row maps need n*(k_max+1) entries")
+    _check(_lib.sv_pack_varlen(_ptr(kept), _ptr(last_token), _ptr(draft_tokens), n, k_max,
+                               _ptr(cu_rows), _ptr(row_req), _ptr(row_pos), _ptr(packed_tokens),
+                               _ptr(dev_error), _stream(stream)),
+           "sv_pack_varlen")
+
+
+_DTYPES = {torch.bfloat16: SV_BF16, torch.float32: SV_F32}
+
+
+def _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
+                 out_tokens, out_accepted, ws, out_p_draft, out_q_draft, out_residual_mass,
+                 dev_error, vocab):
+    if target.dtype not in _DTYPES:
+        raise ValueError("logits must be bfloat16 or float32")
+    _dev(target, target.dtype, "target", 2)
+    if draft is not None:
+        _dev(draft, target.dtype, "draft", 2)
+    _dev(draft_tokens, torch.int32, "draft_tokens", 2)
+    _dev(cu_rows, torch.int32, "cu_rows", 1)
+    _dev(out_tokens, torch.int32, "out_tokens", 2)
+    _dev(out_accepted, torch.int32, "out_accepted", 1)
+    _dev(ws, torch.uint8, "ws", 1)
+    for name, t in (("out_p_draft", out_p_draft), ("out_q_draft", out_q_draft)):
+        _dev(t, torch.float32, name, 2)
+    _dev(out_residual_mass, torch.float32, "out_residual_mass", 1)
+    _dev(dev_error, torch.int32, "dev_error", 1)
+    n, k_max = draft_tokens.shape
+    V = target.shape[1] if vocab is None else int(vocab)
+    if cu_rows.numel() != n + 1 or tuple(out_tokens.shape) != (n, k_max + 1) \
+            or out_accepted.numel() != n:
+        raise ValueError("cu_rows [n+1], out_tokens [n, k_max+1], out_accepted [n]")
+    if draft is not None and draft.shape[0] < n * k_max:
+        raise ValueError("draft must hold n*k_max rows")
+    for t in (out_p_draft, out_q_draft):
+        if t is not None and tuple(t.shape) != (n, k_max):
+            raise ValueError("out_p_draft/out_q_draft must be [n, k_max]")
+    if out_residual_mass is not None and out_residual_mass.numel() != n:
+        raise ValueError("out_residual_mass must have n entries")
+    return [_ptr(target), target.shape[1], target.shape[0], _ptr(draft),
+            0 if draft is None else draft.shape[1], _DTYPES[target.dtype], V,
+            _ptr(draft_tokens), _ptr(cu_rows), n, k_max, int(mode), float(temperature),
+            int(seed), int(step), _ptr(out_tokens), _ptr(out_accepted), _ptr(out_p_draft),
+            _ptr(out_q_draft), _ptr(out_residual_mass), _ptr(dev_error), _ptr(ws), ws.numel()]
+
+
+def sv_verify(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step, out_tokens,
+              out_accepted, ws, out_p_draft=None, out_q_draft=None, out_residual_mass=None,
+              dev_error=None, vocab=None, stream=None):
+    """target [rows, >=V] and draft [n*k_max, >=V] (bf16 or f32, row stride = shape[1]);
+    draft_tokens [n, k_max] i32; cu_rows [n+1] i32; ws: uint8 device buffer of
+    sv_verify_workspace_bytes(n, k_max) bytes."""
+    args = _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
+                        out_tokens, out_accepted, ws, out_p_draft, out_q_draft,
+                        out_residual_mass, dev_error, vocab)
+    _check(_lib.sv_verify(*args, _stream(stream)), "sv_verify")
+
+
+def sv_verify_stages(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
+                     out_tokens, out_accepted, ws, stages, out_p_draft=None, out_q_draft=None,
+                     out_residual_mass=None, dev_error=None, vocab=None, stream=None):
+    """sv_verify restricted to pass 1 (stages=1), pass 2 (stages=2) or both (3)."""
+    args = _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
+                        out_tokens, out_accepted, ws, out_p_draft, out_q_draft,
+                        out_residual_mass, dev_error, vocab)
+    _check(_lib.sv_verify_stages(*args, int(stages), _stream(stream)), "sv_verify_stages")
+
+
+def sv_philox_uniforms(seed, step, u, v, stream=None):
+    """u, v [n, n_pos] f32 <- the uniforms sv_verify draws for (r, j, step)."""
+    _dev(u, torch.float32, "u", 2)
+    _dev(v, torch.float32, "v", 2)
+    n, n_pos = u.shape
+    if tuple(v.shape) != (n, n_pos):
+        raise ValueError("u and v must have the same shape")
+    _check(_lib.sv_philox_uniforms(int(seed), int(step), n, n_pos, _ptr(u), _ptr(v),
+                                   _stream(stream)),
+           "sv_philox_uniforms")
+
+
+# ----------------------------------------------------------------------------
+# Allocating conveniences over the calls above (outputs are new device tensors).
+
+def budget_select(conf, draft_len, cost, t_base, n_bonus, stream=None):
+    dev = conf.device
+    n, k_max = conf.shape
+    kept = torch.empty(n, dtype=torch.int32, device=dev)
+    budget = torch.empty(1, dtype=torch.int32, device=dev)
+    survival = torch.empty(n, k_max, dtype=torch.float32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survival, err, stream)
+    return dict(kept=kept, budget=budget, survival=survival, dev_error=err)
+
+
+def pack_varlen(kept, last_token, draft_tokens, stream=None):
+    dev = kept.device
+    n, k_max = draft_tokens.shape
+    cap = n * (k_max + 1)
+    out = dict(cu_rows=torch.empty(n + 1, dtype=torch.int32, device=dev),
+               row_req=torch.empty(cap, dtype=torch.int32, device=dev),
+               row_pos=torch.empty(cap, dtype=torch.int32, device=dev),
+               packed_tokens=torch.empty(cap, dtype=torch.int32, device=dev),
+               dev_error=torch.zeros(1, dtype=torch.int32, device=dev))
+    sv_pack_varlen(kept, last_token, draft_tokens, out["cu_rows"], out["row_req"],
+                   out["row_pos"], out["packed_tokens"], out["dev_error"], stream)
+    return out
+
+
+def verify(target, draft, draft_tokens, cu_rows, mode, temperature=1.0, seed=0, step=0,
+           vocab=None, stream=None):
+    dev = target.device
+    n, k_max = draft_tokens.shape
+    ws = torch.empty(max(1, sv_verify_workspace_bytes(n, k_max)), dtype=torch.uint8, device=dev)
+    out = dict(tokens=torch.empty(n, k_max + 1, dtype=torch.int32, device=dev),
+               accepted=torch.empty(n, dtype=torch.int32, device=dev),
+               p_draft=torch.empty(n, k_max, dtype=torch.float32, device=dev),
+               q_draft=torch.empty(n, k_max, dtype=torch.float32, device=dev),
+               residual_mass=torch.empty(n, dtype=torch.float32, device=dev),
+               dev_error=torch.zeros(1, dtype=torch.int32, device=dev))
+    sv_verify(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
+              out["tokens"], out["accepted"], ws, out["p_draft"], out["q_draft"],
+              out["residual_mass"], out["dev_error"], vocab, stream)
+    return out

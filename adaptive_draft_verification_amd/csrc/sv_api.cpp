@@ -1,0 +1,160 @@
+// C ABI of libspecverify: host-side validation, then launches on the caller's
+// stream.  Every check here runs before any HIP call, so a rejected call
+// touches neither the device nor any output.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "libspecverify.h"
+#include "sv_launch.h"
+
+namespace {
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+sv_status launched(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sv_status_str(sv_status s) {
+    switch (s) {
+        case SV_OK: return "ok";
+        case SV_ERR_NULL: return "a required pointer is NULL";
+        case SV_ERR_SHAPE: return "a size or stride is out of range";
+        case SV_ERR_DTYPE: return "unknown dtype";
+        case SV_ERR_VALUE: return "a scalar argument is out of range";
+        case SV_ERR_WORKSPACE: return "workspace missing or too small";
+        case SV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    }
+    return "unknown status";
+}
+
+size_t sv_budget_workspace_bytes(int32_t n_req, int32_t k_max) {
+    (void)n_req;
+    (void)k_max;
+    return 0;
+}
+
+size_t sv_verify_workspace_bytes(int32_t n_req, int32_t k_max) {
+    if (n_req < 0 || k_max < 0) return 0;
+    return sv::verify_workspace_bytes(n_req, k_max);
+}
+
+sv_status sv_cost_table_prepare(const float* raw, int32_t raw_len, int32_t granule, float* out,
+                                int32_t out_len) {
+    if (raw == nullptr || out == nullptr) return SV_ERR_NULL;
+    if (granule < 1 || out_len < 1 || raw_len < 1) return SV_ERR_SHAPE;
+    const int64_t last_padded = ((int64_t)(out_len - 1) + granule - 1) / granule * granule;
+    if ((int64_t)raw_len < last_padded + 1) return SV_ERR_SHAPE;
+    for (int32_t t = 0; t < raw_len; ++t)
+        if (!std::isfinite(raw[t]) || !(raw[t] > 0.0f)) return SV_ERR_VALUE;
+    // running maximum up to each padded size, read at ceil_g(t)
+    float running = raw[0];
+    int64_t filled = 0;  // raw entries folded into `running`
+    for (int32_t t = 0; t < out_len; ++t) {
+        const int64_t padded = ((int64_t)t + granule - 1) / granule * granule;
+        while (filled <= padded) {
+            if (raw[filled] > running) running = raw[filled];
+            ++filled;
+        }
+        out[t] = running;
+    }
+    return SV_OK;
+}
+
+sv_status sv_budget_select(const float* conf, const int32_t* draft_len, int32_t n_req,
+                           int32_t k_max, const float* cost, int32_t cost_len, int32_t t_base,
+                           int32_t n_bonus, int32_t* kept, int32_t* budget, float* survival,
+                           int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (n_req < 0 || k_max < 0) return SV_ERR_SHAPE;
+    if (cost == nullptr || budget == nullptr) return SV_ERR_NULL;
+    if (n_req > 0 && (draft_len == nullptr || kept == nullptr)) return SV_ERR_NULL;
+    if (n_req > 0 && k_max > 0 && conf == nullptr) return SV_ERR_NULL;
+    if (n_req > SV_MAX_BUDGET_SLOTS || (int64_t)n_req * k_max > SV_MAX_BUDGET_SLOTS)
+        return SV_ERR_SHAPE;
+    if (t_base < 0 || n_bonus < 0) return SV_ERR_VALUE;
+    if ((int64_t)cost_len < (int64_t)t_base + (int64_t)n_req * k_max + 1) return SV_ERR_SHAPE;
+    return launched(sv::launch_budget(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept,
+                                      budget, survival, dev_error, as_stream(stream)));
+}
+
+sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
+                         const int32_t* draft_tokens, int32_t n_req, int32_t k_max,
+                         int32_t* cu_rows, int32_t* row_req, int32_t* row_pos,
+                         int32_t* packed_tokens, int32_t* dev_error, void* stream) {
+    if (n_req < 0 || k_max < 0) return SV_ERR_SHAPE;
+    if ((int64_t)n_req * (k_max + 1) > INT32_MAX) return SV_ERR_SHAPE;
+    if (cu_rows == nullptr) return SV_ERR_NULL;
+    if (n_req > 0 && (kept == nullptr || last_token == nullptr || row_req == nullptr ||
+                      row_pos == nullptr || packed_tokens == nullptr))
+        return SV_ERR_NULL;
+    if (n_req > 0 && k_max > 0 && draft_tokens == nullptr) return SV_ERR_NULL;
+    return launched(sv::launch_pack(kept, last_token, draft_tokens, n_req, k_max, cu_rows,
+                                    row_req, row_pos, packed_tokens, dev_error,
+                                    as_stream(stream)));
+}
+
+sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t target_rows,
+                           const void* draft_logits, int64_t draft_ld, sv_dtype dtype,
+                           int32_t vocab, const int32_t* draft_tokens, const int32_t* cu_rows,
+                           int32_t n_req, int32_t k_max, sv_mode mode, float temperature,
+                           uint64_t seed, uint64_t step, int32_t* out_tokens,
+                           int32_t* out_accepted, float* out_p_draft, float* out_q_draft,
+                           float* out_residual_mass, int32_t* dev_error, void* ws,
+                           size_t ws_bytes, int32_t stages, void* stream) {
+    if (stages < 1 || stages > 3) return SV_ERR_VALUE;
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
+    if (mode != SV_STOCHASTIC && mode != SV_GREEDY) return SV_ERR_VALUE;
+    if (n_req < 0 || k_max < 0 || k_max > SV_MAX_DRAFT) return SV_ERR_SHAPE;
+    if (vocab < 1 || vocab > SV_MAX_VOCAB) return SV_ERR_SHAPE;
+    if (target_rows < 0 || target_ld < vocab) return SV_ERR_SHAPE;
+    const bool stochastic = mode == SV_STOCHASTIC;
+    if (stochastic && draft_ld < vocab) return SV_ERR_SHAPE;
+    if (stochastic && (!std::isfinite(temperature) || !(temperature > 0.0f))) return SV_ERR_VALUE;
+    if (n_req == 0) return SV_OK;
+    if (target_logits == nullptr || cu_rows == nullptr || out_tokens == nullptr ||
+        out_accepted == nullptr)
+        return SV_ERR_NULL;
+    if (k_max > 0 && draft_tokens == nullptr) return SV_ERR_NULL;
+    if (stochastic && k_max > 0 && draft_logits == nullptr) return SV_ERR_NULL;
+    // the largest element offset a kernel may form must fit int64
+    if ((double)target_rows * (double)target_ld > 9.0e18) return SV_ERR_SHAPE;
+    const size_t need = sv::verify_workspace_bytes(n_req, k_max);
+    if (ws == nullptr || ws_bytes < need) return SV_ERR_WORKSPACE;
+    if (stochastic && (1.4426950408889634 / (double)temperature) > 3.0e38) return SV_ERR_VALUE;
+    sv::VerifyArgs a{target_logits, target_ld,    target_rows,  draft_logits, draft_ld,
+                     dtype,         vocab,        draft_tokens, cu_rows,      n_req,
+                     k_max,         mode,         temperature,  seed,         step,
+                     out_tokens,    out_accepted, out_p_draft,  out_q_draft,  out_residual_mass,
+                     dev_error,     ws,           stages};
+    return launched(sv::launch_verify(a, as_stream(stream)));
+}
+
+sv_status sv_verify(const void* target_logits, int64_t target_ld, int64_t target_rows,
+                    const void* draft_logits, int64_t draft_ld, sv_dtype dtype, int32_t vocab,
+                    const int32_t* draft_tokens, const int32_t* cu_rows, int32_t n_req,
+                    int32_t k_max, sv_mode mode, float temperature, uint64_t seed, uint64_t step,
+                    int32_t* out_tokens, int32_t* out_accepted, float* out_p_draft,
+                    float* out_q_draft, float* out_residual_mass, int32_t* dev_error, void* ws,
+                    size_t ws_bytes, void* stream) {
+    return sv_verify_stages(target_logits, target_ld, target_rows, draft_logits, draft_ld, dtype,
+                            vocab, draft_tokens, cu_rows, n_req, k_max, mode, temperature, seed,
+                            step, out_tokens, out_accepted, out_p_draft, out_q_draft,
+                            out_residual_mass, dev_error, ws, ws_bytes, 3, stream);
+}
+
+sv_status sv_philox_uniforms(uint64_t seed, uint64_t step, int32_t n_req, int32_t n_pos,
+                             float* u, float* v, void* stream) {
+    if (n_req < 0 || n_pos < 0) return SV_ERR_SHAPE;
+    if ((int64_t)n_req * n_pos > 0 && (u == nullptr || v == nullptr)) return SV_ERR_NULL;
+    return launched(sv::launch_philox_uniforms(seed, step, n_req, n_pos, u, v,
+                                               as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Device-side helpers shared by the libspecverify kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "libspecverify.h"
+
+namespace sv {
+
+constexpr int kWave = 64;
+
+// Per-candidate-row statistics written by verify pass 1 and read by pass 2.
+//   a    : offset in the scaled-logit domain, a = max_x z_x * log2(e) / T
+//          (up to rounding), so that exp2(z * c - a) <= ~1;
+//   s    : sum_x exp2(z_x * c - a);
+//   pd   : probability of the position's draft id, exp2(z_d * c - a) / s;
+//   info : greedy -> argmax id; stochastic -> 0; < 0 marks a faulty row.
+struct alignas(16) RowStat {
+    float a;
+    float s;
+    float pd;
+    int32_t info;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Raw v_exp_f32: 2^x, 1 ulp, flushes results below 2^-126 (terms that small
+// do not change an fp32 sum that holds a term >= 1).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Bit-level classification (independent of any fast-math assumptions).
+__device__ __forceinline__ bool is_nan_bits(float x) {
+    return (__float_as_uint(x) & 0x7fffffffu) > 0x7f800000u;
+}
+__device__ __forceinline__ bool is_finite_bits(float x) {
+    return (__float_as_uint(x) & 0x7fffffffu) < 0x7f800000u;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int wave_or_int(int v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o);
+    return v;
+}
+
+// Inclusive wave scan (Hillis-Steele over 64 lanes).
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        T t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11, section 3): per round the products of the two
+// multipliers with counter words 0 and 2 are split in high and low halves,
+// the new counter is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0), and the key
+// advances by the Weyl constants.
+struct Philox4 {
+    uint32_t x0, x1, x2, x3;
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+    constexpr uint32_t kMul0 = 0xD2511F53u, kMul1 = 0xCD9E8D57u;
+    constexpr uint32_t kWeyl0 = 0x9E3779B9u, kWeyl1 = 0xBB67AE85u;
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint32_t hi0 = __umulhi(kMul0, c0), lo0 = kMul0 * c0;
+        const uint32_t hi1 = __umulhi(kMul1, c2), lo1 = kMul1 * c2;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += kWeyl0;
+        k1 += kWeyl1;
+    }
+    return {c0, c1, c2, c3};
+}
+
+// Uniforms of (request, position, step): u from word 0, v from word 1, each
+// the top 24 bits scaled by 2^-24 (exact in fp32).
+__device__ __forceinline__ void draw_uniforms(uint64_t seed, uint64_t step, uint32_t req,
+                                              uint32_t pos, float* u, float* v) {
+    const Philox4 w = philox4x32_10(req, pos, (uint32_t)step, (uint32_t)(step >> 32),
+                                    (uint32_t)seed, (uint32_t)(seed >> 32));
+    *u = (float)(w.x0 >> 8) * 0x1p-24f;
+    *v = (float)(w.x1 >> 8) * 0x1p-24f;
+}
+
+__device__ __forceinline__ void raise_error(int32_t* dev_error, int bits) {
+    if (dev_error != nullptr && bits) atomicOr(dev_error, bits);
+}
+
+}  // namespace sv

@@ -1,0 +1,55 @@
+// Host-side launchers of the libspecverify kernels (internal; the C ABI in
+// sv_api.cpp validates arguments before calling these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "libspecverify.h"
+
+namespace sv {
+
+hipError_t launch_budget(const float* conf, const int32_t* draft_len, int n_req, int k_max,
+                         const float* cost, int t_base, int n_bonus, int32_t* kept,
+                         int32_t* budget, float* survival, int32_t* dev_error,
+                         hipStream_t stream);
+
+hipError_t launch_pack(const int32_t* kept, const int32_t* last_token,
+                       const int32_t* draft_tokens, int n_req, int k_max, int32_t* cu_rows,
+                       int32_t* row_req, int32_t* row_pos, int32_t* packed_tokens,
+                       int32_t* dev_error, hipStream_t stream);
+
+struct VerifyArgs {
+    const void* target;
+    int64_t target_ld;
+    int64_t target_rows;
+    const void* draft;
+    int64_t draft_ld;
+    sv_dtype dtype;
+    int vocab;
+    const int32_t* draft_tokens;
+    const int32_t* cu_rows;
+    int n_req;
+    int k_max;
+    sv_mode mode;
+    float temperature;
+    uint64_t seed;
+    uint64_t step;
+    int32_t* out_tokens;
+    int32_t* out_accepted;
+    float* out_p_draft;
+    float* out_q_draft;
+    float* out_residual_mass;
+    int32_t* dev_error;
+    void* ws;
+    int stages;  // bit 0: pass 1, bit 1: pass 2
+};
+
+size_t verify_workspace_bytes(int n_req, int k_max);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+
+hipError_t launch_philox_uniforms(uint64_t seed, uint64_t step, int n_req, int n_pos, float* u,
+                                  float* v, hipStream_t stream);
+
+}  // namespace sv

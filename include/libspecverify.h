@@ -1,0 +1,252 @@
+/*
+ * libspecverify — the batched speculative-decoding verify step on AMD Instinct
+ * MI355X (gfx950): adaptive budget selection, varlen packing of the kept
+ * rows, and full-vocabulary verification (stochastic or greedy).
+ *
+ * Pages this interface follows (cited by title and section):
+ *  - FOS Study blog "추측 디코딩과 vLLM 적응형 검증" (Speculative decoding and
+ *    vLLM adaptive verification);
+ *  - agentlens "vLLM DSpark을 활용한 적응형 검증(Adaptive Verification)";
+ *  - PyTorch-KR "Hardware-Aware Dynamic Speculative Decoding (DSD), feat.
+ *    Cohere".
+ *
+ * Conventions for every call below.
+ *  - Array arguments are caller-owned DEVICE pointers unless marked "host".
+ *    The library allocates nothing and keeps no state between calls.
+ *  - Every call only enqueues work on `stream` (a hipStream_t passed as an
+ *    opaque pointer; NULL is the default stream) and never synchronises, so
+ *    outputs are valid once the stream has reached that point.
+ *  - The return value reports faults the host can see before anything is
+ *    enqueued (null pointers, sizes, out-of-range scalars, short workspace):
+ *    then nothing is launched and no output is touched.  SV_ERR_LAUNCH means
+ *    the HIP runtime refused a launch.
+ *  - Faults that only the data on the device can show are ORed into
+ *    *dev_error (SV_DEV_* bits below; the library never clears it, so zero it
+ *    before the call).  dev_error may be NULL.  Kernels never read or write
+ *    past the bounds the host validated, whatever the device data holds: the
+ *    crash write-up on the FOS page (section "적응형 검증이 GPU 오류와 엮인
+ *    사례") is about a kernel that trusted a length it was not given.
+ *  - Layouts are row-major; int32 token ids; "-1" marks an empty slot, as the
+ *    -1 placeholders of the DSD page (section "비동기 스케줄링(Async
+ *    Scheduling)과의 호환").
+ */
+#ifndef LIBSPECVERIFY_H
+#define LIBSPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_NULL = 1,      /* a required pointer is NULL                        */
+    SV_ERR_SHAPE = 2,     /* a size or stride is out of range                  */
+    SV_ERR_DTYPE = 3,     /* unknown sv_dtype                                  */
+    SV_ERR_VALUE = 4,     /* a scalar is out of range (temperature, mode, ...) */
+    SV_ERR_WORKSPACE = 5, /* workspace missing or smaller than required        */
+    SV_ERR_LAUNCH = 6     /* the HIP runtime refused a kernel launch           */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+typedef enum { SV_STOCHASTIC = 0, SV_GREEDY = 1 } sv_mode;
+
+/* Device error bits (ORed into *dev_error). */
+#define SV_DEV_BAD_CU_ROWS   1  /* a request's row range is inconsistent or exceeds target_rows */
+#define SV_DEV_BAD_TOKEN     2  /* a kept draft id is outside [0, vocab)                        */
+#define SV_DEV_NONFINITE     4  /* a needed logit row holds NaN or +inf, or only -inf            */
+#define SV_DEV_BAD_DRAFT_LEN 8  /* a draft length is outside [0, k_max] (clamped)                */
+#define SV_DEV_BAD_COST      16 /* a consulted cost entry is not finite and > 0 (never chosen)   */
+#define SV_DEV_BAD_KEPT      32 /* a kept count is outside [0, k_max] (clamped)                  */
+
+/* Limits checked on the host. */
+#define SV_MAX_BUDGET_SLOTS 8192   /* n_req and n_req * k_max for sv_budget_select (LDS-resident) */
+#define SV_MAX_DRAFT        64     /* k_max for sv_verify (one wave64 ballot covers a request)   */
+#define SV_MAX_VOCAB        1048576
+
+const char* sv_status_str(sv_status s);
+
+/*
+ * Workspace bytes the device calls need (0 = none; pass ws = NULL then).
+ * sv_verify keeps one 16-byte statistics record per candidate row.
+ */
+size_t sv_budget_workspace_bytes(int32_t n_req, int32_t k_max);
+size_t sv_verify_workspace_bytes(int32_t n_req, int32_t k_max);
+
+/*
+ * sv_cost_table_prepare — HOST ONLY (no device work).
+ *
+ * agentlens page, section "기술적 구현 및 CUDA Graphs": the engine profiles
+ * the step cost per token count at start-up (item Cost Modeling), forces the
+ * curve to be monotone to absorb profiling noise and tile effects, and prices
+ * a batch at the next captured graph size (item CUDA Graph Padding: 121 tokens
+ * cost what 128 do).  Here: out[t] = max(raw[0 .. ceil_g(t)]) for
+ * t = 0 .. out_len-1, where ceil_g rounds up to a multiple of `granule`
+ * (granule 1 = no padding).
+ *
+ * raw:  host, raw_len fp32 profiled costs, each finite and > 0.
+ * out:  host, out_len fp32 (may not alias raw).
+ * Errors: SV_ERR_NULL; SV_ERR_SHAPE if granule < 1, out_len < 1 or
+ * raw_len < ceil_g(out_len-1) + 1; SV_ERR_VALUE if a raw entry is not finite
+ * and > 0 (out untouched).
+ */
+sv_status sv_cost_table_prepare(const float* raw, int32_t raw_len, int32_t granule,
+                                float* out, int32_t out_len);
+
+/*
+ * sv_budget_select — adaptive verification budget.
+ *
+ * FOS page, section "적응형 검증 > 동작", steps 1-3, and agentlens page,
+ * section "DSpark 신뢰도 스케줄링 메커니즘" (Global Top-B Selection, Budget
+ * Calculation):
+ *  1. survival s[r, j-1] = c[r,0] * ... * c[r,j-1] for draft position
+ *     j = 1..draft_len[r], taken left to right in fp32 (round to nearest),
+ *     each confidence clamped to [0, 1] with NaN read as 0;
+ *  2. every draft slot of the batch ranked by survival, descending; ties to
+ *     the lower request, then the lower position — so each request's kept
+ *     slots are a front prefix;
+ *  3. B = the smallest maximiser over B = 0 .. sum(draft_len) of
+ *     (n_bonus + S(B)) / cost[t_base + B], where S(B) is the sum of the B best
+ *     survivals, taken exactly as sum(floor(s * 2^40)) * 2^-40 and the ratio
+ *     in fp64;
+ *  4. kept[r] = number of request r's slots among the first B.
+ *
+ * conf:      [n_req, k_max] fp32 per-position acceptance estimates.
+ * draft_len: [n_req] int32 drafts written per request (clamped into
+ *            [0, k_max], SV_DEV_BAD_DRAFT_LEN).
+ * cost:      [cost_len] fp32 step cost by token count, already shaped (see
+ *            sv_cost_table_prepare); cost_len >= t_base + n_req*k_max + 1.
+ *            Entries consulted that are not finite and > 0 are never chosen
+ *            (SV_DEV_BAD_COST); if none is usable B = 0.
+ * t_base:    non-draft tokens in the step (one per request for pure decode).
+ * n_bonus:   bonus tokens (one per sampling request).
+ * kept:      [n_req] int32 out.   budget: [1] int32 out (B).
+ * survival:  [n_req, k_max] fp32 out, or NULL (0 past draft_len).
+ * ws:        sv_budget_workspace_bytes(n_req, k_max) bytes (currently 0).
+ * Launch: one workgroup of 1024 threads (LDS-resident sort).
+ * Errors: SV_ERR_NULL; SV_ERR_SHAPE if n_req < 0, k_max < 0,
+ * n_req or n_req * k_max > SV_MAX_BUDGET_SLOTS, or cost_len too short; SV_ERR_VALUE if
+ * t_base < 0 or n_bonus < 0.
+ */
+sv_status sv_budget_select(const float* conf, const int32_t* draft_len, int32_t n_req,
+                           int32_t k_max, const float* cost, int32_t cost_len, int32_t t_base,
+                           int32_t n_bonus, int32_t* kept, int32_t* budget, float* survival,
+                           int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sv_pack_varlen — lay the kept rows out as one varlen decode batch.
+ *
+ * agentlens page, section "기술적 구현 및 CUDA Graphs", item Graph Capture:
+ * one decode shape holds 1 .. k+1 query tokens per request; section "설정 및
+ * 재현": capacity (k + 1) * max_num_seq.  Request r owns rows
+ * cu_rows[r] .. cu_rows[r] + kept[r]; row 0 of a request carries its last
+ * emitted token, row i > 0 draft token i-1.
+ *
+ * kept:          [n_req] int32 (clamped into [0, k_max], SV_DEV_BAD_KEPT).
+ * last_token:    [n_req] int32.   draft_tokens: [n_req, k_max] int32.
+ * cu_rows:       [n_req + 1] int32 out: exclusive scan of kept + 1.
+ * row_req, row_pos, packed_tokens: [n_req * (k_max + 1)] int32 out; rows past
+ *                cu_rows[n_req] hold -1.
+ * Launch: one workgroup.
+ * Errors: SV_ERR_NULL; SV_ERR_SHAPE if n_req < 0 or k_max < 0 or the
+ * capacity overflows int32.
+ */
+sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
+                         const int32_t* draft_tokens, int32_t n_req, int32_t k_max,
+                         int32_t* cu_rows, int32_t* row_req, int32_t* row_pos,
+                         int32_t* packed_tokens, int32_t* dev_error, void* stream);
+
+/*
+ * sv_verify — full-vocabulary verification of every kept row.
+ *
+ * FOS page, section "추측 디코딩이란": drafts are checked from the front and
+ * accepted up to the first mismatch; the target's own token fills the
+ * mismatch, or follows the last draft if all are accepted (bonus token;
+ * section "평균 수락 길이").  Section "속도, 메모리, 정확도에 주는 영향", row
+ * 정확도: with rejection sampling the output law is the target's.
+ *
+ * Stochastic mode, per request r with b = cu_rows[r+1] - cu_rows[r] - 1:
+ *   p_j = softmax(target row j / T), q_j = softmax(draft row j / T);
+ *   (u_j, v_j) = Philox4x32-10 (Salmon et al., SC'11) with key = seed and
+ *   counter = (r, j, step low, step high), u from word 0 and v from word 1 as
+ *   (word >> 8) * 2^-24;
+ *   draft d_j accepted iff u_j * q_j(d_j) < p_j(d_j) (u < min(1, p/q));
+ *   L = first rejected position, else b;
+ *   token at L: if L < b, the smallest id x with C(x) > v_L * W for
+ *   C the running sum of w = max(0, p_L - q_L) and W its total (p_L if W = 0);
+ *   if L = b, the same draw from p_b.
+ * Greedy mode: d_j accepted iff it is the argmax (lowest id on ties) of target
+ *   row j; the token at L is that argmax.  draft_logits may be NULL and
+ *   temperature is ignored.
+ *
+ * target_logits: packed target rows, row cu_rows[r] + j at
+ *                target_logits + (cu_rows[r] + j) * target_ld elements;
+ *                target_rows = rows the buffer holds (a request whose rows
+ *                pass it is a fault, SV_DEV_BAD_CU_ROWS).
+ * draft_logits:  [n_req * k_max] draft rows, row r*k_max + j at stride
+ *                draft_ld elements (stochastic mode).
+ * dtype:         SV_BF16 or SV_F32, same for both.  Rows whose start is
+ *                16-byte aligned take the vector path; others are read
+ *                element-wise (slower, same result).
+ * draft_tokens:  [n_req, k_max] int32 (ids outside [0, vocab) at a kept
+ *                position: SV_DEV_BAD_TOKEN).
+ * cu_rows:       [n_req + 1] int32, as written by sv_pack_varlen.
+ * temperature:   > 0 and finite in stochastic mode.
+ * out_tokens:    [n_req, k_max + 1] int32: accepted drafts, then the token at
+ *                L, then -1.   out_accepted: [n_req] int32 L.
+ * out_p_draft, out_q_draft: [n_req, k_max] fp32 p_j(d_j), q_j(d_j) for j < b,
+ *                -1 elsewhere and in greedy mode; may be NULL.
+ * out_residual_mass: [n_req] fp32 sum max(0, p_L - q_L) when a draft was
+ *                rejected in stochastic mode, else -1; may be NULL.
+ * A faulty request (any SV_DEV_* bit of its own) writes -1 to all of its
+ * outputs.
+ * ws:            sv_verify_workspace_bytes(n_req, k_max) bytes.
+ * Launch: pass 1, one workgroup per candidate row (n_req * (2*k_max + 1)
+ * stochastic, n_req * (k_max + 1) greedy; rows beyond a request's kept count
+ * exit at once); pass 2, one workgroup per request.
+ * Errors: SV_ERR_NULL; SV_ERR_DTYPE; SV_ERR_SHAPE if n_req < 0, k_max outside
+ * [0, SV_MAX_DRAFT], vocab outside [1, SV_MAX_VOCAB], a stride below vocab or
+ * target_rows < 0; SV_ERR_VALUE for an unknown mode or a bad temperature;
+ * SV_ERR_WORKSPACE.
+ */
+sv_status sv_verify(const void* target_logits, int64_t target_ld, int64_t target_rows,
+                    const void* draft_logits, int64_t draft_ld, sv_dtype dtype, int32_t vocab,
+                    const int32_t* draft_tokens, const int32_t* cu_rows, int32_t n_req,
+                    int32_t k_max, sv_mode mode, float temperature, uint64_t seed, uint64_t step,
+                    int32_t* out_tokens, int32_t* out_accepted, float* out_p_draft,
+                    float* out_q_draft, float* out_residual_mass, int32_t* dev_error, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * sv_verify_stages — sv_verify split at its two launches, for callers that
+ * time or schedule the passes separately.  Same arguments and checks as
+ * sv_verify, plus `stages`: 1 = pass 1 only (row statistics into ws),
+ * 2 = pass 2 only (decisions, draws and outputs from the ws that pass 1 of
+ * the same arguments filled earlier on the same stream), 3 = both
+ * (identical to sv_verify).  Errors: as sv_verify; SV_ERR_VALUE if stages is
+ * not 1, 2 or 3.
+ */
+sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t target_rows,
+                           const void* draft_logits, int64_t draft_ld, sv_dtype dtype,
+                           int32_t vocab, const int32_t* draft_tokens, const int32_t* cu_rows,
+                           int32_t n_req, int32_t k_max, sv_mode mode, float temperature,
+                           uint64_t seed, uint64_t step, int32_t* out_tokens,
+                           int32_t* out_accepted, float* out_p_draft, float* out_q_draft,
+                           float* out_residual_mass, int32_t* dev_error, void* ws,
+                           size_t ws_bytes, int32_t stages, void* stream);
+
+/*
+ * sv_philox_uniforms — the (u, v) pairs sv_verify draws, for inspection.
+ * u, v: [n_req, n_pos] fp32 out for counters (r, j, step) with r < n_req,
+ * j < n_pos.  Errors: SV_ERR_NULL; SV_ERR_SHAPE if a size is negative.
+ */
+sv_status sv_philox_uniforms(uint64_t seed, uint64_t step, int32_t n_req, int32_t n_pos,
+                             float* u, float* v, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSPECVERIFY_H */

@@ -182,7 +182,8 @@ def verify(target, draft, draft_tokens, cu_rows, k_max, vocab, mode, temperature
     target = np.asarray(target)
     rows_avail = target.shape[0] if target_rows is None else int(target_rows)
     if draft is not None:
-        draft = np.asarray(draft).reshape(n * k_max, -1)
+        draft = np.asarray(draft)
+        draft = draft.reshape(n * k_max, draft.shape[-1])
     draft_tokens = np.asarray(draft_tokens).reshape(n, k_max)
     tokens = np.full((n, k_max + 1), -1, dtype=np.int32)
     accepted = np.full(n, -1, dtype=np.int32)

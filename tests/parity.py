@@ -1,0 +1,199 @@
+"""Helpers for the GPU-vs-oracle parity tests (not a test module).
+
+Inputs come from the seeded generators in ``workloads``; expected values come
+from ``oracle`` only.  The HIP path is reached through the binding, i.e.
+through the C ABI.
+
+Comparison rules:
+* bit-exact: budget, kept counts, survival bits, cu_rows, row maps, packed
+  tokens, greedy tokens and accepted lengths, device error bits, the accepted
+  draft prefix;
+* p(d), q(d): relative 1e-5, plus two fp32 subnormal ulps (2**-148) for values
+  below fp32's normal range, where relative 1e-5 cannot be represented;
+  residual mass: relative 1e-5 with an absolute floor of 1e-7 (p close to q
+  cancels);
+* a stochastic accept decision may differ only where |u - p/q| < 1e-5 (then
+  the oracle is replayed with the GPU's accepted length and every overridden
+  decision must lie in that band);
+* a stochastic token may differ only where the oracle's v * W lies within
+  1e-5 * W of every cumulative-sum boundary between the two ids, and the
+  GPU's id must carry positive weight.
+"""
+
+import numpy as np
+import torch
+
+import adaptive_draft_verification_amd as sv
+import oracle
+import workloads
+
+U_BAND = 1e-5
+CDF_BAND = 1e-5
+P_RTOL = 1e-5
+RESID_ATOL = 1e-7
+P_ATOL = 2.0 ** -148  # two fp32 subnormal ulps
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(dev())
+
+
+def logits_dtype(w):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+# ------------------------------------------------------------------ budget
+
+def gpu_budget(conf, draft_len, cost, t_base, n_bonus):
+    out = sv.budget_select(to_dev(np.asarray(conf, np.float32)),
+                           to_dev(np.asarray(draft_len, np.int32)),
+                           to_dev(np.asarray(cost, np.float32)), t_base, n_bonus)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def check_budget(conf, draft_len, k_max, cost, t_base, n_bonus):
+    g = gpu_budget(conf, draft_len, cost, t_base, n_bonus)
+    o = oracle.budget_select(conf, draft_len, k_max, cost, t_base, n_bonus)
+    assert int(g["budget"][0]) == o["budget"], (int(g["budget"][0]), o["budget"])
+    np.testing.assert_array_equal(g["kept"], o["kept"])
+    np.testing.assert_array_equal(g["survival"].view(np.uint32), o["survival"].view(np.uint32))
+    assert int(g["dev_error"][0]) == o["dev_error"]
+    return o
+
+
+# -------------------------------------------------------------------- pack
+
+def check_pack(kept, last_token, draft_tokens, k_max):
+    draft_tokens = np.asarray(draft_tokens, np.int32).reshape(len(kept), k_max)
+    g = sv.pack_varlen(to_dev(np.asarray(kept, np.int32)), to_dev(np.asarray(last_token, np.int32)),
+                       to_dev(draft_tokens))
+    torch.cuda.synchronize()
+    o = oracle.pack_varlen(kept, last_token, draft_tokens, k_max)
+    for key in ("cu_rows", "row_req", "row_pos", "packed_tokens"):
+        np.testing.assert_array_equal(g[key].cpu().numpy(), o[key], err_msg=key)
+    assert int(g["dev_error"].cpu()[0]) == o["dev_error"]
+    return o
+
+
+# ------------------------------------------------------------------ verify
+
+def gpu_verify(target, draft, draft_tokens, cu_rows, k_max, mode, tau, dtype, seed=0, step=0,
+               vocab=None, target_ld=None, draft_ld=None):
+    """Run sv_verify on host arrays (fp32 holding the exact logit values).
+
+    target_ld / draft_ld > vocab place rows at a wider stride (the extra
+    columns hold NaN that must never be read)."""
+    V = target.shape[1] if vocab is None else vocab
+
+    def widen(a, ld):
+        if ld is None or ld == a.shape[1]:
+            return a
+        out = np.full((a.shape[0], ld), np.nan, dtype=np.float32)
+        out[:, : a.shape[1]] = a
+        return out
+
+    t = to_dev(widen(target, target_ld), dtype)
+    d = None if draft is None else to_dev(widen(draft, draft_ld), dtype)
+    out = sv.verify(t, d, to_dev(np.asarray(draft_tokens, np.int32)),
+                    to_dev(np.asarray(cu_rows, np.int32)),
+                    sv.SV_GREEDY if mode == "greedy" else sv.SV_STOCHASTIC, tau, seed, step,
+                    vocab=V)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def compare_verify(g, target, draft, draft_tokens, cu_rows, k_max, vocab, mode, tau, seed=0,
+                   step=0):
+    """Check GPU outputs against the oracle; returns counts of band cases."""
+    om = oracle.GREEDY if mode == "greedy" else oracle.STOCHASTIC
+    o = oracle.verify(target, draft, draft_tokens, cu_rows, k_max, vocab, om, tau, seed, step)
+    stats = dict(requests=len(cu_rows) - 1, u_band=0, cdf_band=0, degenerate=0)
+    assert int(g["dev_error"][0]) == o["dev_error"], (int(g["dev_error"][0]), o["dev_error"])
+    n = len(cu_rows) - 1
+    draft_tokens = np.asarray(draft_tokens).reshape(n, k_max)
+    if mode == "greedy":
+        np.testing.assert_array_equal(g["tokens"], o["tokens"])
+        np.testing.assert_array_equal(g["accepted"], o["accepted"])
+        assert (g["p_draft"] == -1).all() and (g["q_draft"] == -1).all()
+        assert (g["residual_mass"] == -1).all()
+        return stats
+    for r in range(n):
+        res = o["per_request"][r]
+        if res is None or res["fault"]:
+            assert g["accepted"][r] == -1 and (g["tokens"][r] == -1).all()
+            assert (g["p_draft"][r] == -1).all() and (g["q_draft"][r] == -1).all()
+            assert g["residual_mass"][r] == -1
+            continue
+        b = int(cu_rows[r + 1] - cu_rows[r] - 1)
+        # probabilities of the draft ids
+        np.testing.assert_allclose(g["p_draft"][r, :b], res["p_d"], rtol=P_RTOL, atol=P_ATOL,
+                                   err_msg=f"p(d) request {r}")
+        np.testing.assert_allclose(g["q_draft"][r, :b], res["q_d"], rtol=P_RTOL, atol=P_ATOL,
+                                   err_msg=f"q(d) request {r}")
+        assert (g["p_draft"][r, b:] == -1).all() and (g["q_draft"][r, b:] == -1).all()
+        Lg = int(g["accepted"][r])
+        assert 0 <= Lg <= b
+        replayed = Lg != res["L"]
+        if replayed:
+            # first differing decision must sit in the u band; replay with the GPU's L
+            rep = oracle.verify_request(r, _rows_t(target, cu_rows, r, b),
+                                        _rows_d(draft, r, k_max, b), draft_tokens[r], b, vocab,
+                                        om, tau, seed, step, forced_l=Lg)
+            assert rep["overridden"], r
+            for _j, gap in rep["overridden"]:
+                assert gap < U_BAND, (r, _j, gap)
+            stats["u_band"] += 1
+            res = rep
+        # accepted prefix is the draft ids themselves
+        np.testing.assert_array_equal(g["tokens"][r, :Lg], draft_tokens[r, :Lg])
+        assert (g["tokens"][r, Lg + 1:] == -1).all()
+        gt, ot = int(g["tokens"][r, Lg]), int(res["tokens"][Lg])
+        if Lg < b:
+            want = res["residual_mass"]
+            assert abs(g["residual_mass"][r] - want) <= max(P_RTOL * want, RESID_ATOL), \
+                (r, g["residual_mass"][r], want)
+        else:
+            assert g["residual_mass"][r] == -1
+        if gt != ot:
+            if replayed and Lg < b and res["residual_mass"] < 1e-3:
+                stats["degenerate"] += 1  # near-empty residual after a band decision
+                continue
+            full = oracle.verify_request(r, _rows_t(target, cu_rows, r, b),
+                                         _rows_d(draft, r, k_max, b), draft_tokens[r], b, vocab,
+                                         om, tau, seed, step, forced_l=Lg, keep_weights=True)
+            w, v = full["weights"], full["v"]
+            c = np.cumsum(w)
+            t = v * c[-1]
+            lo, hi = min(gt, ot), max(gt, ot)
+            assert 0 <= gt < vocab and w[gt] > 0, (r, gt)
+            assert np.all(np.abs(c[lo:hi] - t) <= CDF_BAND * c[-1]), (r, gt, ot)
+            stats["cdf_band"] += 1
+    return stats
+
+
+def _rows_t(target, cu_rows, r, b):
+    lo = int(cu_rows[r])
+    return [target[lo + j] for j in range(b + 1)]
+
+
+def _rows_d(draft, r, k_max, b):
+    if draft is None:
+        return []
+    return [draft[r * k_max + j] for j in range(b)]
+
+
+def workload_inputs(w, kept, mode):
+    """Packed target, padded draft, draft ids and cu_rows (oracle pack) for `kept`."""
+    toks = w.draft_tokens(mode)
+    pk = oracle.pack_varlen(kept, w.last_token, toks, w.k_max)
+    target = workloads.assemble_target(w, pk["cu_rows"], kept)
+    draft = workloads.assemble_draft(w, kept) if mode != "greedy" else None
+    return target, draft, toks, pk["cu_rows"]

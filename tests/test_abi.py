@@ -1,0 +1,175 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, rejects bad host arguments before touching the device, and its
+host-only cost-table call matches the oracle bit for bit.  No device compute
+is launched here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libspecverify.h")
+
+sv = pytest.importorskip("adaptive_draft_verification_amd",
+                         reason="libspecverify.so not built (python adaptive_draft_verification_amd/build.py)")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "sv_verify" in names and "sv_budget_select" in names and "sv_pack_varlen" in names
+    lib = ctypes.CDLL(sv.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(sv.EXPORTED) == names
+
+
+def test_status_strings():
+    for s in range(7):
+        assert sv.sv_status_str(s)
+    assert sv.sv_status_str(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert sv.sv_verify_workspace_bytes(256, 7) == 256 * 15 * 16
+    assert sv.sv_verify_workspace_bytes(-1, 7) == 0
+    assert sv.sv_budget_workspace_bytes(256, 7) == 0
+
+
+@pytest.mark.parametrize("granule", [1, 2, 16])
+def test_cost_table_prepare_matches_oracle(granule):
+    rng = np.random.default_rng(granule)
+    raw = (1 + rng.uniform(0, 1, 4097) * np.linspace(1, 5, 4097)).astype(np.float32)
+    out_len = 4097 - granule
+    got = sv.sv_cost_table_prepare(raw, granule, out_len)
+    want = oracle.cost_table_prepare(raw, granule, out_len)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_cost_table_prepare_errors():
+    raw = np.ones(10, dtype=np.float32)
+    with pytest.raises(sv.SvError) as e:
+        sv.sv_cost_table_prepare(raw, 16, 10)
+    assert e.value.status == sv.SV_ERR_SHAPE
+    bad = raw.copy()
+    bad[4] = np.inf
+    with pytest.raises(sv.SvError) as e:
+        sv.sv_cost_table_prepare(bad, 1, 5)
+    assert e.value.status == sv.SV_ERR_VALUE
+    with pytest.raises(sv.SvError) as e:
+        sv.sv_cost_table_prepare(raw, 0, 5)
+    assert e.value.status == sv.SV_ERR_SHAPE
+    lib = sv._lib
+    assert lib.sv_cost_table_prepare(None, 10, 1, FAKE, 5) == sv.SV_ERR_NULL
+
+
+def budget(**kw):
+    args = dict(conf=FAKE, draft_len=FAKE, n_req=4, k_max=3, cost=FAKE, cost_len=17, t_base=4,
+                n_bonus=4, kept=FAKE, budget=FAKE, survival=None, dev_error=None, ws=None,
+                ws_bytes=0, stream=None)
+    args.update(kw)
+    return sv._lib.sv_budget_select(*args.values())
+
+
+def test_budget_select_host_validation():
+    assert budget(cost_len=16) == sv.SV_ERR_SHAPE          # needs t_base + n*k + 1
+    assert budget(n_req=-1) == sv.SV_ERR_SHAPE
+    assert budget(k_max=-2) == sv.SV_ERR_SHAPE
+    assert budget(n_req=2048, k_max=5, cost_len=20000) == sv.SV_ERR_SHAPE  # > 8192 slots
+    assert budget(n_req=8193, k_max=0, cost_len=20000) == sv.SV_ERR_SHAPE  # > 8192 requests
+    assert budget(t_base=-1) == sv.SV_ERR_VALUE
+    assert budget(n_bonus=-1) == sv.SV_ERR_VALUE
+    assert budget(cost=None) == sv.SV_ERR_NULL
+    assert budget(budget=None) == sv.SV_ERR_NULL
+    assert budget(conf=None) == sv.SV_ERR_NULL
+    assert budget(kept=None) == sv.SV_ERR_NULL
+
+
+def pack(**kw):
+    args = dict(kept=FAKE, last_token=FAKE, draft_tokens=FAKE, n_req=4, k_max=3, cu_rows=FAKE,
+                row_req=FAKE, row_pos=FAKE, packed=FAKE, dev_error=None, stream=None)
+    args.update(kw)
+    return sv._lib.sv_pack_varlen(*args.values())
+
+
+def test_pack_host_validation():
+    assert pack(n_req=-1) == sv.SV_ERR_SHAPE
+    assert pack(k_max=-1) == sv.SV_ERR_SHAPE
+    assert pack(n_req=2**30, k_max=7) == sv.SV_ERR_SHAPE
+    for key in ("kept", "last_token", "draft_tokens", "cu_rows", "row_req", "row_pos", "packed"):
+        assert pack(**{key: None}) == sv.SV_ERR_NULL, key
+
+
+def verify(**kw):
+    args = dict(target=FAKE, target_ld=32, target_rows=16, draft=FAKE, draft_ld=32,
+                dtype=sv.SV_F32, vocab=32, draft_tokens=FAKE, cu_rows=FAKE, n_req=4, k_max=3,
+                mode=sv.SV_STOCHASTIC, temperature=1.0, seed=0, step=0, out_tokens=FAKE,
+                out_accepted=FAKE, out_p=None, out_q=None, out_resid=None, dev_error=None,
+                ws=FAKE, ws_bytes=4 * 7 * 16, stream=None)
+    args.update(kw)
+    return sv._lib.sv_verify(*args.values())
+
+
+def test_verify_host_validation():
+    assert verify(dtype=7) == sv.SV_ERR_DTYPE
+    assert verify(mode=5) == sv.SV_ERR_VALUE
+    assert verify(n_req=-1) == sv.SV_ERR_SHAPE
+    assert verify(k_max=65) == sv.SV_ERR_SHAPE
+    assert verify(vocab=0) == sv.SV_ERR_SHAPE
+    assert verify(vocab=2**20 + 1, target_ld=2**21, draft_ld=2**21) == sv.SV_ERR_SHAPE
+    assert verify(target_ld=31) == sv.SV_ERR_SHAPE
+    assert verify(draft_ld=31) == sv.SV_ERR_SHAPE
+    assert verify(target_rows=-1) == sv.SV_ERR_SHAPE
+    assert verify(temperature=0.0) == sv.SV_ERR_VALUE
+    assert verify(temperature=-1.0) == sv.SV_ERR_VALUE
+    assert verify(temperature=float("nan")) == sv.SV_ERR_VALUE
+    assert verify(temperature=float("inf")) == sv.SV_ERR_VALUE
+    assert verify(temperature=1e-39) == sv.SV_ERR_VALUE
+    assert verify(ws_bytes=4 * 7 * 16 - 1) == sv.SV_ERR_WORKSPACE
+    assert verify(ws=None) == sv.SV_ERR_WORKSPACE
+    for key in ("target", "cu_rows", "out_tokens", "out_accepted", "draft_tokens", "draft"):
+        assert verify(**{key: None}) == sv.SV_ERR_NULL, key
+    # greedy needs no draft logits, no draft stride and no temperature; it then
+    # fails only on the (deliberately) missing workspace, still before any launch
+    assert verify(mode=sv.SV_GREEDY, draft=None, draft_ld=0, temperature=0.0,
+                  ws=None) == sv.SV_ERR_WORKSPACE
+    # nothing to do: OK without touching anything
+    assert verify(n_req=0, target=None, ws=None) == sv.SV_OK
+
+
+def test_verify_stages_validation():
+    base = dict(target=FAKE, target_ld=32, target_rows=16, draft=FAKE, draft_ld=32,
+                dtype=sv.SV_F32, vocab=32, draft_tokens=FAKE, cu_rows=FAKE, n_req=4, k_max=3,
+                mode=sv.SV_STOCHASTIC, temperature=1.0, seed=0, step=0, out_tokens=FAKE,
+                out_accepted=FAKE, out_p=None, out_q=None, out_resid=None, dev_error=None,
+                ws=FAKE, ws_bytes=4 * 7 * 16)
+    for bad in (0, 4, -1):
+        assert sv._lib.sv_verify_stages(*base.values(), bad, None) == sv.SV_ERR_VALUE
+    base["ws"] = None
+    for ok in (1, 2, 3):
+        assert sv._lib.sv_verify_stages(*base.values(), ok, None) == sv.SV_ERR_WORKSPACE
+
+
+def test_philox_host_validation():
+    assert sv._lib.sv_philox_uniforms(0, 0, -1, 3, FAKE, FAKE, None) == sv.SV_ERR_SHAPE
+    assert sv._lib.sv_philox_uniforms(0, 0, 2, 3, None, FAKE, None) == sv.SV_ERR_NULL
+    assert sv._lib.sv_philox_uniforms(0, 0, 0, 3, None, None, None) == sv.SV_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    conf = torch.zeros(2, 2)
+    with pytest.raises(ValueError):
+        sv.budget_select(conf, torch.zeros(2, dtype=torch.int32), torch.ones(9), 2, 2)

@@ -1,0 +1,316 @@
+"""GPU (HIP, through the C ABI) versus the oracle, on seeded synthetic inputs.
+
+Sizes: the five workloads at their real shapes (tiny, 16 x V32000,
+64 x V128256, 256 x V129280, 256 x mixed K up to 15 x V256000), plus ragged
+vocabularies, unaligned strides, several pass-2 tiles and the degenerate
+cases (no drafts, empty batch, faults, masked logits, the exact fallback).
+The comparison rules are in tests/parity.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+from parity import (check_budget, check_pack, compare_verify, gpu_verify, logits_dtype, to_dev,
+                    workload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import adaptive_draft_verification_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ Philox
+
+def test_philox_bit_equal_to_oracle():
+    import adaptive_draft_verification_amd as sv
+    for seed, step, n, npos in [(0, 0, 256, 16), (2**63 + 12345, 2**40 + 7, 300, 65),
+                                (123, 5, 4096, 8)]:
+        u = torch.empty(n, npos, dtype=torch.float32, device="cuda")
+        v = torch.empty_like(u)
+        sv.sv_philox_uniforms(seed, step, u, v)
+        torch.cuda.synchronize()
+        r = np.repeat(np.arange(n), npos)
+        j = np.tile(np.arange(npos), n)
+        ou, ov = oracle.uniforms(seed, r, j, step)
+        np.testing.assert_array_equal(u.cpu().numpy().ravel(), ou.astype(np.float32))
+        np.testing.assert_array_equal(v.cpu().numpy().ravel(), ov.astype(np.float32))
+
+
+# ------------------------------------------------------------------ budget
+
+@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
+def test_budget_workloads(name):
+    w = workloads.make(name)
+    cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+    o = check_budget(w.conf, w.draft_len, w.k_max, cost, w.t_base, w.n_bonus)
+    log(f"{name}: B={o['budget']} kept rows={int(o['kept'].sum()) + w.n}")
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_budget_random(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 300))
+    k = int(rng.integers(1, min(16, 8192 // n) + 1))
+    conf, dl, cost, t_base, n_bonus = workloads.random_budget_case(
+        rng, n, k, ties=seed % 2 == 0, zeros=seed % 3 == 0, flat_cost=seed % 7 == 0)
+    if seed % 5 == 0:
+        cost = np.maximum.accumulate(cost)
+    if seed % 11 == 0:  # out-of-range draft lengths and bad confidences
+        dl[0] = k + 3
+        dl[-1] = -2
+        conf[0, 0] = np.nan
+        conf[-1, -1] = 7.0
+    if seed % 13 == 0:  # some unusable cost entries
+        cost[t_base + 1] = np.nan
+        cost[-1] = 0.0
+    check_budget(conf, dl, k, cost, t_base, n_bonus)
+
+
+@pytest.mark.parametrize("n,k", [(8192, 1), (1024, 8), (512, 16), (128, 64), (1, 1), (3, 0),
+                                 (0, 4)])
+def test_budget_edges(n, k):
+    rng = np.random.default_rng(n + k)
+    conf = rng.uniform(0.3, 1.0, (n, k)).astype(np.float32)
+    dl = rng.integers(0, k + 1, n).astype(np.int32)
+    t = np.arange(n + n * k + 1, dtype=np.float32)
+    cost = np.maximum(1.0, t / max(1, n)).astype(np.float32)
+    check_budget(conf, dl, k, cost, n, n)
+
+
+def test_budget_denormal_survivals():
+    conf = np.full((4, 6), 2.0 ** -30, dtype=np.float32)
+    conf[:, 0] = 0.5
+    dl = np.full(4, 6, dtype=np.int32)
+    cost = np.ones(4 + 24 + 1, dtype=np.float32)
+    check_budget(conf, dl, 6, cost, 4, 4)
+
+
+# -------------------------------------------------------------------- pack
+
+@pytest.mark.parametrize("seed", range(12))
+def test_pack_random(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(0, 3000))
+    k = int(rng.integers(0, 16))
+    kept = rng.integers(0, k + 1, n)
+    if seed % 4 == 0 and n:
+        kept[0] = k + 5  # clamped, flagged
+        kept[-1] = -1
+    check_pack(kept, rng.integers(0, 1000, n), rng.integers(0, 1000, (n, k)), k)
+
+
+# ------------------------------------------------------------------ verify
+
+def run_workload_verify(name, mode, adaptive):
+    w = workloads.make(name)
+    if adaptive:
+        cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+        kept = oracle.budget_select(w.conf, w.draft_len, w.k_max, cost, w.t_base,
+                                    w.n_bonus)["kept"]
+    else:
+        kept = w.draft_len.copy()
+    target, draft, toks, cu = workload_inputs(w, kept, mode)
+    log(f"{name} {mode} adaptive={adaptive}: rows={int(cu[-1])} V={w.vocab}")
+    g = gpu_verify(target, draft, toks, cu, w.k_max, mode, w.tau, logits_dtype(w),
+                   seed=w.seed, step=w.step)
+    stats = compare_verify(g, target, draft, toks, cu, w.k_max, w.vocab, mode, w.tau, w.seed,
+                           w.step)
+    log(f"  {stats}")
+    w.drop_cache()
+    return g, stats
+
+
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+@pytest.mark.parametrize("name,adaptive", [("tiny", True), ("tiny", False),
+                                           ("b16_v32000", False), ("b64_v128256", True)])
+def test_verify_small_workloads(name, adaptive, mode):
+    run_workload_verify(name, mode, adaptive)
+
+
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_verify_b64_full_k(mode):
+    run_workload_verify("b64_v128256", mode, False)
+
+
+@pytest.mark.parametrize("adaptive", [True, False])
+def test_verify_b256_v129280_stochastic(adaptive):
+    g, stats = run_workload_verify("b256_v129280", "stochastic", adaptive)
+    assert stats["u_band"] + stats["cdf_band"] <= 3
+
+
+def test_verify_b256_v129280_greedy():
+    run_workload_verify("b256_v129280", "greedy", False)
+
+
+def test_verify_b256_mix_v256000():
+    run_workload_verify("b256_mix_v256000", "stochastic", True)
+
+
+# ------------------------------------------------------- shapes and edge cases
+
+def synthetic(rng, n, k, V, kept=None, scale=3.0):
+    kept = rng.integers(0, k + 1, n) if kept is None else np.asarray(kept)
+    cu = np.concatenate([[0], np.cumsum(kept + 1)]).astype(np.int32)
+    target = (rng.standard_normal((int(cu[-1]), V)) * scale).astype(np.float32)
+    draft = np.full((n * k, V), np.nan, dtype=np.float32)
+    toks = np.full((n, k), -1, dtype=np.int32)
+    for r in range(n):
+        for j in range(int(kept[r])):
+            row = target[cu[r] + j] + rng.standard_normal(V).astype(np.float32)
+            draft[r * k + j] = row
+            toks[r, j] = int(np.argmax(row - np.log(rng.standard_exponential(V))))
+    return target, draft, toks, cu
+
+
+def bf16_round(a):
+    return torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V,ld_pad", [(1003, 0), (20001, 0), (32, 3), (8192 * 3 + 5, 1),
+                                      (1, 0), (7, 0)])
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_verify_ragged_vocab_and_strides(dtype, V, ld_pad, mode):
+    rng = np.random.default_rng(V + ld_pad)
+    n, k = 9, 4
+    target, draft, toks, cu = synthetic(rng, n, k, V)
+    if dtype == torch.bfloat16:
+        target, draft = bf16_round(target), bf16_round(draft)
+    log(f"ragged V={V} ld_pad={ld_pad} {dtype} {mode}")
+    g = gpu_verify(target, draft if mode == "stochastic" else None, toks, cu, k, mode, 0.8,
+                   dtype, seed=3, step=11, target_ld=V + ld_pad, draft_ld=V + ld_pad)
+    compare_verify(g, target, draft if mode == "stochastic" else None, toks, cu, k, V, mode, 0.8,
+                   3, 11)
+
+
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_verify_no_drafts(mode):
+    rng = np.random.default_rng(5)
+    n, V = 6, 4000
+    target = (rng.standard_normal((n, V)) * 3).astype(np.float32)
+    cu = np.arange(n + 1, dtype=np.int32)
+    toks = np.zeros((n, 0), dtype=np.int32)
+    draft = np.zeros((0, V), dtype=np.float32) if mode == "stochastic" else None
+    g = gpu_verify(target, draft, toks, cu, 0, mode, 1.0, torch.float32)
+    compare_verify(g, target, draft, toks, cu, 0, V, mode, 1.0)
+    assert (g["accepted"] == 0).all()
+
+
+def test_verify_empty_batch():
+    import adaptive_draft_verification_amd as sv
+    out = sv.verify(torch.zeros(1, 8, device="cuda"), torch.zeros(1, 8, device="cuda"),
+                    torch.zeros(0, 2, dtype=torch.int32, device="cuda"),
+                    torch.zeros(1, dtype=torch.int32, device="cuda"), sv.SV_STOCHASTIC)
+    torch.cuda.synchronize()
+    assert out["tokens"].numel() == 0 and int(out["dev_error"].item()) == 0
+
+
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+def test_verify_faults_and_masks(mode):
+    rng = np.random.default_rng(17)
+    n, k, V = 8, 3, 5000
+    kept = np.array([3, 3, 3, 3, 2, 1, 0, 3])
+    target, draft, toks, cu = synthetic(rng, n, k, V, kept)
+    target[cu[1] + 1, 77] = np.nan                 # request 1: NaN in a target row
+    toks[2, 1] = V + 4                             # request 2: draft id out of range
+    draft[3 * k + 2, :] = -np.inf                  # request 3: draft row without mass
+    target[cu[4] + 0, : V // 2] = -np.inf          # request 4: masked half row (legal)
+    target[cu[5] + 1, 4000] = np.inf               # request 5: +inf logit
+    target[cu[7] + 2, :] = -np.inf                 # request 7: target row without mass
+    dmode = draft if mode == "stochastic" else None
+    g = gpu_verify(target, dmode, toks, cu, k, mode, 1.0, torch.float32)
+    compare_verify(g, target, dmode, toks, cu, k, V, mode, 1.0)
+    assert g["accepted"][4] >= 0
+    assert int(g["dev_error"][0]) != 0
+
+
+def test_verify_bad_offsets_never_read_past_target_rows():
+    rng = np.random.default_rng(23)
+    n, k, V = 5, 2, 3000
+    target, draft, toks, cu = synthetic(rng, n, k, V, [2, 2, 2, 2, 2])
+    bad = cu.copy()
+    bad[2] = bad[1] - 1       # request 1 negative length, request 2 too long
+    bad[5] = bad[5] + 4       # request 4 runs past the buffer
+    for mode in ("stochastic", "greedy"):
+        dmode = draft if mode == "stochastic" else None
+        g = gpu_verify(target, dmode, toks, bad, k, mode, 1.0, torch.float32)
+        compare_verify(g, target, dmode, toks, bad, k, V, mode, 1.0)
+        assert int(g["dev_error"][0]) & oracle.DEV_BAD_CU_ROWS
+
+
+def test_verify_exact_fallback_for_late_large_logit():
+    """A logit far above the first chunk's maximum forces the exact two-pass path."""
+    rng = np.random.default_rng(29)
+    n, k, V = 4, 2, 70000
+    target, draft, toks, cu = synthetic(rng, n, k, V, [2, 2, 2, 2])
+    target[cu[1] + 0, V - 3] = 180.0
+    draft[2 * k + 1, 65000] = 150.0
+    target[cu[3] + 2, 5:] -= 120.0
+    for dtype in (torch.float32, torch.bfloat16):
+        t = target if dtype == torch.float32 else bf16_round(target)
+        d = draft if dtype == torch.float32 else bf16_round(draft)
+        g = gpu_verify(t, d, toks, cu, k, "stochastic", 1.0, dtype, seed=9)
+        compare_verify(g, t, d, toks, cu, k, V, "stochastic", 1.0, 9)
+
+
+def test_verify_low_temperature_and_ties():
+    rng = np.random.default_rng(31)
+    n, k, V = 16, 4, 9000
+    target, draft, toks, cu = synthetic(rng, n, k, V)
+    target = np.round(target)  # many exact ties
+    draft = np.round(draft)
+    for tau in (0.05, 3.0):
+        g = gpu_verify(target, draft, toks, cu, k, "stochastic", tau, torch.float32, seed=2)
+        compare_verify(g, target, draft, toks, cu, k, V, "stochastic", tau, 2)
+    g = gpu_verify(target, None, toks, cu, k, "greedy", 1.0, torch.float32)
+    compare_verify(g, target, None, toks, cu, k, V, "greedy", 1.0)
+
+
+def test_verify_is_deterministic_and_stream_safe():
+    rng = np.random.default_rng(37)
+    n, k, V = 32, 7, 50000
+    target, draft, toks, cu = synthetic(rng, n, k, V)
+    a = gpu_verify(target, draft, toks, cu, k, "stochastic", 1.0, torch.bfloat16, seed=4, step=2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = gpu_verify(target, draft, toks, cu, k, "stochastic", 1.0, torch.bfloat16, seed=4,
+                       step=2)
+    torch.cuda.synchronize()
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+    c = gpu_verify(target, draft, toks, cu, k, "stochastic", 1.0, torch.bfloat16, seed=4, step=3)
+    assert not np.array_equal(a["tokens"], c["tokens"])
+
+
+def test_end_to_end_path_on_device():
+    """budget -> pack -> verify, each stage reading the previous stage's device output."""
+    import adaptive_draft_verification_amd as sv
+    w = workloads.make("b64_v128256")
+    cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+    o_b = oracle.budget_select(w.conf, w.draft_len, w.k_max, cost, w.t_base, w.n_bonus)
+    toks = w.draft_tokens("stochastic")
+    o_p = oracle.pack_varlen(o_b["kept"], w.last_token, toks, w.k_max)
+    target = workloads.assemble_target(w, o_p["cu_rows"], o_b["kept"])
+    draft = workloads.assemble_draft(w, o_b["kept"])
+    dt = logits_dtype(w)
+    b = sv.budget_select(to_dev(w.conf), to_dev(w.draft_len), to_dev(cost), w.t_base, w.n_bonus)
+    p = sv.pack_varlen(b["kept"], to_dev(w.last_token), to_dev(toks))
+    v = sv.verify(to_dev(target, dt), to_dev(draft, dt), to_dev(toks), p["cu_rows"],
+                  sv.SV_STOCHASTIC, w.tau, w.seed, w.step)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(p["cu_rows"].cpu().numpy(), o_p["cu_rows"])
+    g = {k: t.cpu().numpy() for k, t in v.items()}
+    compare_verify(g, target, draft, toks, o_p["cu_rows"], w.k_max, w.vocab, "stochastic", w.tau,
+                   w.seed, w.step)

@@ -105,8 +105,8 @@ class Workload:
         tok_s = np.full(self.k_max, -1, dtype=np.int32)
         tok_g = np.full(self.k_max, -1, dtype=np.int32)
         for j in range(K):
-            e = gs.standard_exponential(V, dtype=np.float32)
-            race = zd[j].astype(np.float64) / self.tau - np.log(e.astype(np.float64))
+            e = gs.standard_exponential(V)
+            race = zd[j].astype(np.float64) / self.tau - np.log(e)
             tok_s[j] = int(np.argmax(race))
             tok_g[j] = int(np.argmax(zd[j]))
         out = dict(target=z, draft=zd, tok_stochastic=tok_s, tok_greedy=tok_g)
