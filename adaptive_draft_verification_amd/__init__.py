@@ -267,7 +267,7 @@ def verify(target, draft, draft_tokens, cu_rows, mode, temperature=1.0, seed=0, 
            vocab=None, stream=None):
     dev = target.device
     n, k_max = draft_tokens.shape
-    ws = torch.empty(max(1, sv_verify_workspace_bytes(n, k_max)), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(1, sv_verify_workspace_bytes(n, k_max)), dtype=torch.uint8, device=dev)
     out = dict(tokens=torch.empty(n, k_max + 1, dtype=torch.int32, device=dev),
                accepted=torch.empty(n, dtype=torch.int32, device=dev),
                p_draft=torch.empty(n, k_max, dtype=torch.float32, device=dev),

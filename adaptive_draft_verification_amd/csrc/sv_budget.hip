@@ -5,12 +5,21 @@
 // Verification)", section "DSpark 신뢰도 스케줄링 메커니즘" (Global Top-B
 // Selection, Budget Calculation).
 //
-// At most SV_MAX_BUDGET_SLOTS draft slots: the whole problem lives in LDS.
-//   1. survival products per request (one thread walks one request's
-//      positions in order, fp32 round-to-nearest, no contraction);
-//   2. 64-bit keys (~survival bits << 32 | slot id) sorted ascending by a
-//      bitonic network in LDS: descending survival, then request, then
-//      position — a total order, so the sort is deterministic;
+// At most SV_MAX_BUDGET_SLOTS draft slots, so the whole problem lives on one
+// CU:
+//   0. every global input is requested up front (confidences, draft lengths,
+//      and the cost entries of this thread's ranks) so their latencies
+//      overlap;
+//   1. one thread per request forms the survival products in position order
+//      (fp32 round-to-nearest, no contraction) and writes that request's
+//      keys — (bits that fall as survival rises) << 32 | slot id, unique —
+//      as one ascending run: survival never rises with position, so every
+//      request's run is already sorted;
+//   2. a merge tree joins the runs pairwise, ceil(log2 n) levels, two LDS
+//      buffers in turn: each key lands at (its index in its run) + (number of
+//      keys below it in the partner run), found by one binary search — exact
+//      and order free because keys are unique.  The order is survival
+//      descending, then request, then position;
 //   3. fixed-point prefix sums sum floor(s * 2^40) in uint64 (exact, order
 //      free), fp64 scores (n_bonus + S * 2^-40) / cost[t_base + B], and the
 //      first maximiser;
@@ -23,16 +32,42 @@ namespace {
 
 constexpr int kBudgetThreads = 1024;
 constexpr int kBudgetWaves = kBudgetThreads / kWave;
+// Keys of slots past a request's draft length: above every real key (whose
+// high word is at most 0x7fffffff), unique through the slot id.
+constexpr uint64_t kPadKey = 0x8000000000000000ull;
 
 __device__ __forceinline__ float clamp_confidence(float c) {
-    // NaN and negatives -> 0, above 1 -> 1 (the test below is false for NaN).
-    if (!(c >= 0.0f)) return 0.0f;
+    // NaN, negatives and -0 -> +0; above 1 -> 1.
+    if (!(c > 0.0f)) return 0.0f;
     return c > 1.0f ? 1.0f : c;
 }
 
-// Block-wide exclusive scan of one uint64 per thread; returns the exclusive
-// prefix and writes the block total to *total.
-__device__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* wave_tot, uint64_t* total) {
+// Survival s in [0, 1] -> high key word that grows as s falls (s >= +0).
+__device__ __forceinline__ uint64_t survival_key(float s, int slot) {
+    return ((uint64_t)(0x7fffffffu - __float_as_uint(s)) << 32) | (uint32_t)slot;
+}
+
+__device__ __forceinline__ float key_survival(uint64_t key) {
+    return __uint_as_float(0x7fffffffu - (uint32_t)(key >> 32));
+}
+
+// Number of keys in seg[0 .. len) below `key` (seg ascending, keys unique).
+__device__ __forceinline__ int lower_bound(const uint64_t* seg, int len, uint64_t key) {
+    int lo = 0;
+    while (len > 0) {
+        const int half = len >> 1;
+        if (seg[lo + half] < key) {
+            lo += half + 1;
+            len -= half + 1;
+        } else {
+            len = half;
+        }
+    }
+    return lo;
+}
+
+// Block-wide exclusive scan of one uint64 per thread.
+__device__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* wave_tot) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const uint64_t incl = wave_incl_scan<uint64_t>(v, lane);
@@ -41,122 +76,147 @@ __device__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* wave_tot, uint64_t
     if (wave == 0) {
         uint64_t t = lane < kBudgetWaves ? wave_tot[lane] : 0ull;
         t = wave_incl_scan<uint64_t>(t, lane);
-        if (lane < kBudgetWaves) wave_tot[lane] = t;  // inclusive totals per wave
+        if (lane < kBudgetWaves) wave_tot[lane] = t;
     }
     __syncthreads();
-    const uint64_t before_wave = wave == 0 ? 0ull : wave_tot[wave - 1];
-    *total = wave_tot[kBudgetWaves - 1];
-    return before_wave + incl - v;
+    return (wave == 0 ? 0ull : wave_tot[wave - 1]) + incl - v;
 }
 
+// E = ranks per thread (contiguous), n_req * k_max <= 1024 * E.
+template <int E>
 __global__ __launch_bounds__(kBudgetThreads) void budget_kernel(
     const float* __restrict__ conf, const int32_t* __restrict__ draft_len, int n_req, int k_max,
     const float* __restrict__ cost, int t_base, int n_bonus, int32_t* __restrict__ kept,
     int32_t* __restrict__ budget, float* __restrict__ survival, int32_t* dev_error) {
-    __shared__ uint64_t keys[SV_MAX_BUDGET_SLOTS];
-    __shared__ int32_t kept_s[SV_MAX_BUDGET_SLOTS];
+    __shared__ uint64_t buf[2][SV_MAX_BUDGET_SLOTS];
     __shared__ uint64_t wave_tot[kBudgetWaves];
-    __shared__ int32_t total_slots_s;
-    __shared__ int32_t err_s;
     __shared__ double best_score_s[kBudgetWaves];
     __shared__ int32_t best_b_s[kBudgetWaves];
+    __shared__ int32_t total_slots_s, err_s;
 
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const int n_slots = n_req * k_max;
-    int npow2 = 1;
-    while (npow2 < n_slots) npow2 <<= 1;
+    const int first_rank = tid * E;
+    float* conf_s = reinterpret_cast<float*>(buf[1]);  // staging, dead before buf[1] is used
 
+    // 0. requests for every global input this thread will need
+    float cst[E];
+#pragma unroll
+    for (int q = 0; q < E; ++q) {
+        const int rank = first_rank + q;
+        cst[q] = rank < n_slots ? cost[t_base + rank + 1] : 1.0f;
+    }
+    const float cost0 = cost[t_base];
+    constexpr int kMaxReqPerThread = SV_MAX_BUDGET_SLOTS / kBudgetThreads;
+    int dl[kMaxReqPerThread];
+#pragma unroll
+    for (int i = 0; i < kMaxReqPerThread; ++i) {
+        const int r = tid + i * kBudgetThreads;
+        dl[i] = r < n_req ? draft_len[r] : 0;
+    }
+    for (int i = tid; i < n_slots; i += kBudgetThreads) conf_s[i] = conf[i];
     if (tid == 0) {
         total_slots_s = 0;
         err_s = 0;
     }
     __syncthreads();
 
-    // 1. survival and keys
-    int my_err = 0;
-    int my_total = 0;
-    for (int r = tid; r < n_req; r += kBudgetThreads) {
-        int K = draft_len[r];
+    // 1. survival products and the per-request sorted runs of keys (buf[0])
+    int my_err = 0, my_total = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxReqPerThread; ++i) {
+        const int r = tid + i * kBudgetThreads;
+        if (r >= n_req) break;
+        int K = dl[i];
         if (K < 0 || K > k_max) {
             my_err |= SV_DEV_BAD_DRAFT_LEN;
             K = K < 0 ? 0 : k_max;
         }
         my_total += K;
-        kept_s[r] = 0;
         float s = 1.0f;
         for (int j = 0; j < k_max; ++j) {
             const int slot = r * k_max + j;
             if (j < K) {
-                s = __fmul_rn(s, clamp_confidence(conf[slot]));
-                keys[slot] = ((uint64_t)(0xffffffffu - __float_as_uint(s)) << 32) | (uint32_t)slot;
-                if (survival) survival[slot] = s;
+                s = __fmul_rn(s, clamp_confidence(conf_s[slot]));
+                buf[0][slot] = survival_key(s, slot);
+                if (survival != nullptr) survival[slot] = s;
             } else {
-                keys[slot] = ~0ull;
-                if (survival) survival[slot] = 0.0f;
+                buf[0][slot] = kPadKey | (uint32_t)slot;
+                if (survival != nullptr) survival[slot] = 0.0f;
             }
         }
     }
-    for (int i = n_slots + tid; i < npow2; i += kBudgetThreads) keys[i] = ~0ull;
     if (my_total) atomicAdd(&total_slots_s, my_total);
+    // cost entries are checked here so their loads complete under this phase
+    int cost_bad = 0;
+#pragma unroll
+    for (int q = 0; q < E; ++q) cost_bad |= (cst[q] > 0.0f && is_finite_bits(cst[q])) ? 0 : 1 << q;
+    const bool cost0_bad = !(cost0 > 0.0f && is_finite_bits(cost0));
     if (my_err) atomicOr(&err_s, my_err);
     __syncthreads();
 
-    // 2. bitonic sort, ascending
-    for (int k = 2; k <= npow2; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < (npow2 >> 1); i += kBudgetThreads) {
-                const int lo = 2 * i - (i & (j - 1));
-                const int hi = lo + j;
-                const bool ascending = (lo & k) == 0;
-                const uint64_t x = keys[lo], y = keys[hi];
-                if ((x > y) == ascending) {
-                    keys[lo] = y;
-                    keys[hi] = x;
+    // 2. merge tree over runs of k_max << level slots
+    int src = 0;
+    for (int run = k_max; run < n_slots; run <<= 1) {
+        const uint64_t* in = buf[src];
+        uint64_t* out = buf[src ^ 1];
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+            const int p = first_rank + q;
+            if (p < n_slots) {
+                const uint64_t key = in[p];
+                const int r_idx = p / run;
+                const int pair_base = (r_idx & ~1) * run;
+                const int partner = (r_idx ^ 1) * run;
+                int pos = p - pair_base;  // own index in run, plus left run if right
+                if (partner < n_slots) {
+                    const int plen = min(run, n_slots - partner);
+                    pos = (p - r_idx * run) + lower_bound(in + partner, plen, key);
                 }
+                out[pair_base + pos] = key;
             }
-            __syncthreads();
         }
+        src ^= 1;
+        __syncthreads();
     }
+    const uint64_t* sorted = buf[src];
+    int32_t* kept_s = reinterpret_cast<int32_t*>(buf[src ^ 1]);
+    for (int r = tid; r < n_req; r += kBudgetThreads) kept_s[r] = 0;
 
-    // 3. fixed-point prefix sums over ranks, scores, first maximiser.
-    // Thread t owns the contiguous ranks [t*per, (t+1)*per).
+    // 3. fixed-point prefix sums over ranks, scores, first maximiser
     const int total = total_slots_s;
-    const int per = (npow2 + kBudgetThreads - 1) / kBudgetThreads;
-    const int first = tid * per;
+    uint64_t fx[E];
     uint64_t local = 0;
-    for (int q = 0; q < per; ++q) {
-        const int rank = first + q;
-        if (rank < total) {
-            const float sv = __uint_as_float(0xffffffffu - (uint32_t)(keys[rank] >> 32));
-            local += (uint64_t)(sv * 0x1p40f);  // exact scaling, truncation = floor
-        }
+#pragma unroll
+    for (int q = 0; q < E; ++q) {
+        fx[q] = 0;
+        if (first_rank + q < total) fx[q] = (uint64_t)(key_survival(sorted[first_rank + q]) * 0x1p40f);
+        local += fx[q];  // exact scaling; truncation = floor
     }
-    uint64_t block_total;
-    uint64_t run = block_excl_scan_u64(local, wave_tot, &block_total);
+    uint64_t run_sum = block_excl_scan_u64(local, wave_tot);
 
     double best = -__builtin_inf();
     int best_b = 0x7fffffff;
     int cost_err = 0;
     if (tid == 0) {  // B = 0
-        const float c0 = cost[t_base];
-        if (c0 > 0.0f && is_finite_bits(c0)) {
-            best = (double)n_bonus / (double)c0;
-        } else {
+        if (!cost0_bad)
+            best = (double)n_bonus / (double)cost0;
+        else
             cost_err = SV_DEV_BAD_COST;
-        }
         best_b = 0;
     }
-    for (int q = 0; q < per; ++q) {
-        const int rank = first + q;
+#pragma unroll
+    for (int q = 0; q < E; ++q) {
+        const int rank = first_rank + q;
         if (rank < total) {
-            const float sv = __uint_as_float(0xffffffffu - (uint32_t)(keys[rank] >> 32));
-            run += (uint64_t)(sv * 0x1p40f);
+            run_sum += fx[q];
             const int b = rank + 1;
-            const float cb = cost[t_base + b];
             double sc = -__builtin_inf();
-            if (cb > 0.0f && is_finite_bits(cb)) {
-                sc = __dadd_rn((double)n_bonus, __dmul_rn((double)run, 0x1p-40));
-                sc = __ddiv_rn(sc, (double)cb);
+            if (!((cost_bad >> q) & 1)) {
+                sc = __dadd_rn((double)n_bonus, __dmul_rn((double)run_sum, 0x1p-40));
+                sc = __ddiv_rn(sc, (double)cst[q]);
             } else {
                 cost_err = SV_DEV_BAD_COST;
             }
@@ -166,9 +226,6 @@ __global__ __launch_bounds__(kBudgetThreads) void budget_kernel(
             }
         }
     }
-    // block argmax: larger score, then smaller B
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) {
         const double ob = __shfl_xor(best, o);
@@ -202,10 +259,9 @@ __global__ __launch_bounds__(kBudgetThreads) void budget_kernel(
     const int B = best_b_s[0];
 
     // 4. kept counts
-    for (int rank = tid; rank < B; rank += kBudgetThreads) {
-        const int slot = (int)(uint32_t)keys[rank];
-        atomicAdd(&kept_s[slot / k_max], 1);
-    }
+#pragma unroll
+    for (int q = 0; q < E; ++q)
+        if (first_rank + q < B) atomicAdd(&kept_s[(int)(uint32_t)sorted[first_rank + q] / k_max], 1);
     __syncthreads();
     for (int r = tid; r < n_req; r += kBudgetThreads) kept[r] = kept_s[r];
     if (tid == 0) {
@@ -214,14 +270,34 @@ __global__ __launch_bounds__(kBudgetThreads) void budget_kernel(
     }
 }
 
+template <int E>
+void launch_e(const float* conf, const int32_t* draft_len, int n_req, int k_max,
+              const float* cost, int t_base, int n_bonus, int32_t* kept, int32_t* budget,
+              float* survival, int32_t* dev_error, hipStream_t stream) {
+    hipLaunchKernelGGL(budget_kernel<E>, dim3(1), dim3(kBudgetThreads), 0, stream, conf,
+                       draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
+                       dev_error);
+}
+
 }  // namespace
 
 hipError_t launch_budget(const float* conf, const int32_t* draft_len, int n_req, int k_max,
                          const float* cost, int t_base, int n_bonus, int32_t* kept,
                          int32_t* budget, float* survival, int32_t* dev_error,
                          hipStream_t stream) {
-    hipLaunchKernelGGL(budget_kernel, dim3(1), dim3(kBudgetThreads), 0, stream, conf, draft_len,
-                       n_req, k_max, cost, t_base, n_bonus, kept, budget, survival, dev_error);
+    const int n_slots = n_req * k_max;
+    if (n_slots <= kBudgetThreads)
+        launch_e<1>(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
+                    dev_error, stream);
+    else if (n_slots <= 2 * kBudgetThreads)
+        launch_e<2>(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
+                    dev_error, stream);
+    else if (n_slots <= 4 * kBudgetThreads)
+        launch_e<4>(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
+                    dev_error, stream);
+    else
+        launch_e<8>(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
+                    dev_error, stream);
     return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ struct VerifyArgs {
     float* out_residual_mass;
     int32_t* dev_error;
     void* ws;
-    int stages;  // bit 0: pass 1, bit 1: pass 2
+    int stages;  // bit 0: pass 1 (row statistics), bit 1: pass 2 (decide and draw)
 };
 
 size_t verify_workspace_bytes(int n_req, int k_max);

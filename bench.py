@@ -2,8 +2,9 @@
 
 A step is one pass of the whole path on one batch: adaptive budget selection
 (sv_budget_select), varlen packing (sv_pack_varlen) and full-vocabulary
-verification (sv_verify: pass 1 row statistics, pass 2 decisions and draws),
-each stage reading the previous stage's device output.  The default workload
+verification (sv_verify: row statistics, then each request's decisions and
+draw by the last of its workgroups), each stage reading the previous stage's
+device output.  The default workload
 is 256 requests with 7 drafts each over a 129280-token vocabulary, bf16
 logits, confidences X^j with X ~ Beta(8, 2), and a cost table padded to
 multiples of 16 tokens (workloads.make("b256_v129280")); the budget decides
@@ -13,8 +14,11 @@ Inputs are generated once on the host and copied to HBM before timing; two
 replicas of the logit buffers alternate between steps so that reads come from
 HBM rather than the 256 MB Infinity Cache.  HIP events on the launch stream
 time every stage; `value` is target rows verified per second of whole-step
-time.  A second leg verifies every draft (full K: 2048 target + 1792 draft
-rows) for the bandwidth figure at the largest size.  The CPU oracle runs one
+time, and the roofline is pass 1's algorithmic bytes (every kept row once)
+over its event time; pass 2's bytes (the rows each draw reads again) are
+reported beside it.  A second
+leg verifies every draft (full K: 2048 target + 1792 draft rows) for the
+bandwidth figure at the largest size.  The CPU oracle runs one
 step of the same workload on the host for the cpu_baseline figure.
 
 Prints one JSON line.
@@ -110,7 +114,7 @@ def main():
     row_req = torch.empty(cap, dtype=torch.int32, device=dev)
     row_pos = torch.empty(cap, dtype=torch.int32, device=dev)
     packed = torch.empty(cap, dtype=torch.int32, device=dev)
-    ws = torch.empty(sv.sv_verify_workspace_bytes(n, K), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(sv.sv_verify_workspace_bytes(n, K), dtype=torch.uint8, device=dev)
     tok_out = torch.empty(n, K + 1, dtype=torch.int32, device=dev)
     acc_out = torch.empty(n, dtype=torch.int32, device=dev)
     p_out = torch.empty(n, K, dtype=torch.float32, device=dev)
@@ -137,52 +141,64 @@ def main():
         replicas.append((tp, dr))
     torch.cuda.synchronize()
 
-    def step(i, events=None):
-        tp, dr = replicas[i % len(replicas)]
-        if events is not None:
-            events[0].record(stream)
-        sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, kept, budget, survival,
-                            err)
-        if events is not None:
-            events[1].record(stream)
-        sv.sv_pack_varlen(kept, last_d, toks_d, cu, row_req, row_pos, packed, err)
-        if events is not None:
-            events[2].record(stream)
-        sv.sv_verify_stages(tp, dr, toks_d, cu, mode, w.tau, w.seed, i, tok_out, acc_out, ws, 1,
-                            p_out, q_out, res_out, err, vocab=V)
-        if events is not None:
-            events[3].record(stream)
-        sv.sv_verify_stages(tp, dr, toks_d, cu, mode, w.tau, w.seed, i, tok_out, acc_out, ws, 2,
-                            p_out, q_out, res_out, err, vocab=V)
-        if events is not None:
-            events[4].record(stream)
+    def step(i, events=None, reps=None, cu_rows=None, kept_in=None):
+        """One step; events (5) bracket budget, pack, verify pass 1, verify pass 2."""
+        tp, dr = (reps or replicas)[i % len(reps or replicas)]
+        cu_i = cu if cu_rows is None else cu_rows
+
+        def mark(k):
+            if events is not None:
+                events[k].record(stream)
+
+        mark(0)
+        if kept_in is None:
+            sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, kept, budget,
+                                survival, err)
+        mark(1)
+        if kept_in is None:
+            sv.sv_pack_varlen(kept, last_d, toks_d, cu, row_req, row_pos, packed, err)
+        mark(2)
+        for stage in (1, 2):
+            sv.sv_verify_stages(tp, dr, toks_d, cu_i, mode, w.tau, w.seed, i, tok_out, acc_out,
+                                ws, stage, p_out, q_out, res_out, err, vocab=V)
+            mark(2 + stage)
+
+    def pass2_rows(steps, kept_h_, **kw):
+        """Rows the draws re-read in each of `steps` (deterministic: same step index,
+        same draws): two per rejected request, one per request that accepted all."""
+        if mode == sv.SV_GREEDY:
+            return np.zeros(len(steps))
+        out = []
+        for i in steps:
+            step(i, **kw)
+            acc = acc_out.cpu().numpy()
+            rej = int(((acc >= 0) & (acc < kept_h_)).sum())
+            out.append(2 * rej + (n - rej))
+        return np.array(out, dtype=np.float64)
+
+    def timed(iters, **kw):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(iters)]
+        torch.cuda.synchronize()
+        t0_ = time.perf_counter()
+        for i in range(iters):
+            step(i, ev[i], **kw)
+        torch.cuda.synchronize()
+        wall_ = time.perf_counter() - t0_
+        ms = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(4)]
+                       for i in range(iters)])
+        if int(err.item()) != 0:
+            raise RuntimeError(f"device error bits {int(err.item())} during the benchmark")
+        return wall_, ms
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    stage_ms = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(4)]
-                         for i in range(args.steps)])
-    gpu_step_ms = np.array([ev[i][0].elapsed_time(ev[i][4]) for i in range(args.steps)])
-    if int(err.item()) != 0:
-        raise RuntimeError(f"device error bits {int(err.item())} during the benchmark")
-    # pass-2 bytes depend on the draws (a rejection re-reads two rows, an
-    # all-accepted request one): take them from one more step
-    step(args.steps)
-    torch.cuda.synchronize()
-    acc_h = acc_out.cpu().numpy()
-    n_rejected = int(((acc_h >= 0) & (acc_h < kept_h)).sum())
+    wall, stage_ms = timed(args.steps)
+    p2_rows = pass2_rows(range(args.steps), kept_h)
 
     ms_per_step = wall * 1e3 / args.steps
-    pass1_ms = float(np.mean(stage_ms[:, 2]))
+    pass1_ms, pass2_ms = float(np.mean(stage_ms[:, 2])), float(np.mean(stage_ms[:, 3]))
     pass1_bytes = (rows_t + (rows_d if mode == sv.SV_STOCHASTIC else 0)) * V * esize
-    pass2_bytes = (n_rejected * 2 + (n - n_rejected)) * V * esize if mode == sv.SV_STOCHASTIC \
-        else 0
+    pass2_bytes = float(np.mean(p2_rows)) * V * esize
     achieved = pass1_bytes / (pass1_ms * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- full K leg
@@ -195,41 +211,24 @@ def main():
             full_reps.append((tgt_full_d.clone(), replicas[1][1]))
         rows_tf = int(cu_full[-1].item())
         rows_df = int(w.draft_len.sum())
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-               for _ in range(args.full_k_iters)]
+        kw = dict(reps=full_reps, cu_rows=cu_full, kept_in=True)
         for i in range(3):
-            tp, dr = full_reps[i % len(full_reps)]
-            sv.sv_verify(tp, dr, toks_d, cu_full, mode, w.tau, w.seed, i, tok_out, acc_out, ws,
-                         p_out, q_out, res_out, err, vocab=V)
-        torch.cuda.synchronize()
-        for i in range(args.full_k_iters):
-            tp, dr = full_reps[i % len(full_reps)]
-            fev[i][0].record(stream)
-            sv.sv_verify_stages(tp, dr, toks_d, cu_full, mode, w.tau, w.seed, i, tok_out,
-                                acc_out, ws, 1, p_out, q_out, res_out, err, vocab=V)
-            fev[i][1].record(stream)
-            sv.sv_verify_stages(tp, dr, toks_d, cu_full, mode, w.tau, w.seed, i, tok_out,
-                                acc_out, ws, 2, p_out, q_out, res_out, err, vocab=V)
-            fev[i][2].record(stream)
-        torch.cuda.synchronize()
-        f1 = float(np.mean([fev[i][0].elapsed_time(fev[i][1]) for i in range(args.full_k_iters)]))
-        f2 = float(np.mean([fev[i][1].elapsed_time(fev[i][2]) for i in range(args.full_k_iters)]))
-        fbytes = (rows_tf + (rows_df if mode == sv.SV_STOCHASTIC else 0)) * V * esize
-        acc_f = acc_out.cpu().numpy()
-        nrej_f = int(((acc_f >= 0) & (acc_f < w.draft_len)).sum())
-        fbytes2 = (nrej_f * 2 + (n - nrej_f)) * V * esize if mode == sv.SV_STOCHASTIC else 0
+            step(i, **kw)
+        _, fms = timed(args.full_k_iters, **kw)
+        f1, f2 = float(np.mean(fms[:, 2])), float(np.mean(fms[:, 3]))
+        f_p1 = (rows_tf + (rows_df if mode == sv.SV_STOCHASTIC else 0)) * V * esize
+        f_p2 = float(np.mean(pass2_rows(range(args.full_k_iters), w.draft_len, **kw))) * V * esize
         full = {
             "target_rows": rows_tf, "draft_rows": rows_df if mode == sv.SV_STOCHASTIC else 0,
             "pass1_us": round(f1 * 1e3, 2), "pass2_us": round(f2 * 1e3, 2),
-            "pass1_gbps": round(fbytes / (f1 * 1e-3) / 1e9, 1),
-            "pass1_frac": round(fbytes / (f1 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "verify_gbps": round((fbytes + fbytes2) / ((f1 + f2) * 1e-3) / 1e9, 1),
-            "verify_frac": round((fbytes + fbytes2) / ((f1 + f2) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "pass1_bytes": int(f_p1), "pass2_bytes": int(f_p2),
+            "pass1_gbps": round(f_p1 / (f1 * 1e-3) / 1e9, 1),
+            "pass1_frac": round(f_p1 / (f1 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "verify_gbps": round((f_p1 + f_p2) / ((f1 + f2) * 1e-3) / 1e9, 1),
+            "verify_frac": round((f_p1 + f_p2) / ((f1 + f2) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "verify_rows_per_s": round(rows_tf / ((f1 + f2) * 1e-3), 1),
             "iters": args.full_k_iters,
         }
-        if int(err.item()) != 0:
-            raise RuntimeError(f"device error bits {int(err.item())} in the full-K leg")
 
     # ------------------------------------------------------------ CPU oracle leg
     cpu = None
@@ -276,12 +275,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None, "kernel": "rowstats_kernel (verify pass 1)",
-                     "bytes_per_launch": pass1_bytes},
+                     "bytes_per_launch": int(pass1_bytes)},
         "budget_select_us": round(float(np.mean(stage_ms[:, 0])) * 1e3, 2),
         "pack_us": round(float(np.mean(stage_ms[:, 1])) * 1e3, 2),
         "verify_pass1_us": round(pass1_ms * 1e3, 2),
-        "verify_pass2_us": round(float(np.mean(stage_ms[:, 3])) * 1e3, 2),
-        "gpu_step_us": round(float(np.mean(gpu_step_ms)) * 1e3, 2),
+        "verify_pass2_us": round(pass2_ms * 1e3, 2),
+        "verify_pass2_bytes": int(pass2_bytes),
+        "gpu_step_us": round(float(np.mean(stage_ms.sum(axis=1))) * 1e3, 2),
         "step_hbm_gbps": round((pass1_bytes + pass2_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
         "full_k": full,
         "cpu_baseline": cpu,

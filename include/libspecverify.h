@@ -172,7 +172,9 @@ sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
  *   (u_j, v_j) = Philox4x32-10 (Salmon et al., SC'11) with key = seed and
  *   counter = (r, j, step low, step high), u from word 0 and v from word 1 as
  *   (word >> 8) * 2^-24;
- *   draft d_j accepted iff u_j * q_j(d_j) < p_j(d_j) (u < min(1, p/q));
+ *   draft d_j accepted iff u_j < min(1, p_j(d_j) / q_j(d_j)), the ratio taken
+ *   as 2^(log2 p - log2 q) so that it stays exact-to-rounding when p or q
+ *   falls below fp32's normal range (q = 0 accepts iff p > 0);
  *   L = first rejected position, else b;
  *   token at L: if L < b, the smallest id x with C(x) > v_L * W for
  *   C the running sum of w = max(0, p_L - q_L) and W its total (p_L if W = 0);
@@ -202,10 +204,13 @@ sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
  *                rejected in stochastic mode, else -1; may be NULL.
  * A faulty request (any SV_DEV_* bit of its own) writes -1 to all of its
  * outputs.
- * ws:            sv_verify_workspace_bytes(n_req, k_max) bytes.
- * Launch: pass 1, one workgroup per candidate row (n_req * (2*k_max + 1)
- * stochastic, n_req * (k_max + 1) greedy; rows beyond a request's kept count
- * exit at once); pass 2, one workgroup per request.
+ * ws:            sv_verify_workspace_bytes(n_req, k_max) bytes (per-row
+ *                statistics passed from the first launch to the second).
+ *                Calls that overlap in time must not share a workspace.
+ * Launch: two kernels.  Pass 1: one 256-thread workgroup per candidate row
+ * (n_req * (2*k_max + 1) stochastic, n_req * (k_max + 1) greedy; rows beyond
+ * a request's kept count do nothing).  Pass 2: one workgroup per request
+ * (1024 threads stochastic, 64 greedy) decides and draws.
  * Errors: SV_ERR_NULL; SV_ERR_DTYPE; SV_ERR_SHAPE if n_req < 0, k_max outside
  * [0, SV_MAX_DRAFT], vocab outside [1, SV_MAX_VOCAB], a stride below vocab or
  * target_rows < 0; SV_ERR_VALUE for an unknown mode or a bad temperature;
@@ -221,10 +226,10 @@ sv_status sv_verify(const void* target_logits, int64_t target_ld, int64_t target
 
 /*
  * sv_verify_stages — sv_verify split at its two launches, for callers that
- * time or schedule the passes separately.  Same arguments and checks as
+ * time or schedule the passes on their own.  Same arguments and checks as
  * sv_verify, plus `stages`: 1 = pass 1 only (row statistics into ws),
- * 2 = pass 2 only (decisions, draws and outputs from the ws that pass 1 of
- * the same arguments filled earlier on the same stream), 3 = both
+ * 2 = pass 2 only (decisions, draws and outputs from the ws that a pass 1
+ * with the same arguments filled earlier on the same stream), 3 = both
  * (identical to sv_verify).  Errors: as sv_verify; SV_ERR_VALUE if stages is
  * not 1, 2 or 3.
  */

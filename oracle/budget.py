@@ -40,10 +40,11 @@ def clamp_confidence(c):
 
     The FOS page (section "동작", step 1) treats the estimate as the chance
     that this position is accepted given the earlier ones, i.e. a
-    probability.  NaN and negative values become 0; values above 1 become 1.
+    probability.  NaN, negative values and -0 become +0; values above 1
+    become 1.
     """
     c = np.float32(c)
-    if np.isnan(c) or c < 0:
+    if np.isnan(c) or c <= 0:  # a probability carries no sign: -0 becomes +0 too
         return np.float32(0.0)
     if c > 1:
         return np.float32(1.0)

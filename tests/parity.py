@@ -17,7 +17,10 @@ Comparison rules:
   decision must lie in that band);
 * a stochastic token may differ only where the oracle's v * W lies within
   1e-5 * W of every cumulative-sum boundary between the two ids, and the
-  GPU's id must carry positive weight.
+  GPU's id must carry positive weight;
+* a residual whose oracle mass is below the mass floor (1e-7) is empty to
+  fp32, so the zero-mass fallback (a draw from p at that row) may apply: the
+  GPU's id then only has to lie in p's support.
 """
 
 import numpy as np
@@ -163,6 +166,13 @@ def compare_verify(g, target, draft, draft_tokens, cu_rows, k_max, vocab, mode, 
         else:
             assert g["residual_mass"][r] == -1
         if gt != ot:
+            if Lg < b and res["residual_mass"] < RESID_ATOL:
+                # numerically empty residual (below the mass floor, beyond fp32):
+                # the zero-mass fallback draws from p at that row instead
+                p_l = oracle.row_probs(target[int(cu_rows[r]) + Lg, :vocab], tau)
+                assert 0 <= gt < vocab and p_l[gt] > 0, (r, gt)
+                stats["degenerate"] += 1
+                continue
             if replayed and Lg < b and res["residual_mass"] < 1e-3:
                 stats["degenerate"] += 1  # near-empty residual after a band decision
                 continue

@@ -278,6 +278,25 @@ def test_verify_low_temperature_and_ties():
     compare_verify(g, target, None, toks, cu, k, V, "greedy", 1.0)
 
 
+def test_verify_draw_lands_on_positive_weight():
+    """Residuals with zero weight on every other id, drawn many times: every
+    drawn id must carry weight (the oracle's rule never lands on a zero)."""
+    rng = np.random.default_rng(41)
+    n, k, V = 64, 1, 40000
+    target = (rng.standard_normal((2 * n, V)) * 2).astype(np.float32)
+    cu = np.arange(0, 2 * n + 1, 2, dtype=np.int32)
+    draft = target[0::2].copy()
+    draft[:, 1::2] += 3.0  # q > p on odd ids: zero residual weight there
+    toks = np.ones((n, k), dtype=np.int32)  # an odd id: mostly rejected
+    for step in range(6):
+        g = gpu_verify(target, draft, toks, cu, k, "stochastic", 1.0, torch.float32, seed=5,
+                       step=step)
+        compare_verify(g, target, draft, toks, cu, k, V, "stochastic", 1.0, 5, step)
+        rej = g["accepted"] == 0
+        assert rej.sum() > n // 4
+        assert (g["tokens"][rej, 0] % 2 == 0).all()
+
+
 def test_verify_is_deterministic_and_stream_safe():
     rng = np.random.default_rng(37)
     n, k, V = 32, 7, 50000
