@@ -122,8 +122,10 @@ def sv_cost_table_prepare(raw, granule, out_len):
 
 
 def sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survival=None,
-                     dev_error=None, stream=None):
-    """conf [n, k_max] f32, draft_len [n] i32, cost [L] f32 -> kept [n] i32, budget [1] i32."""
+                     dev_error=None, stream=None, ws=None):
+    """conf [n, k_max] f32, draft_len [n] i32, cost [L] f32 -> kept [n] i32, budget [1] i32.
+
+    ws: device uint8 tensor of at least sv_budget_workspace_bytes(n, k_max) bytes."""
     _dev(conf, torch.float32, "conf", 2)
     _dev(draft_len, torch.int32, "draft_len", 1)
     _dev(cost, torch.float32, "cost", 1)
@@ -131,6 +133,7 @@ def sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survi
     _dev(budget, torch.int32, "budget", 1)
     _dev(survival, torch.float32, "survival", 2)
     _dev(dev_error, torch.int32, "dev_error", 1)
+    _dev(ws, torch.uint8, "ws", 1)
     n, k_max = conf.shape
     if draft_len.numel() != n or kept.numel() != n or budget.numel() < 1:
         raise ValueError("draft_len, kept must have n entries and budget one")
@@ -138,7 +141,8 @@ def sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survi
         raise ValueError("survival must be [n, k_max]")
     _check(_lib.sv_budget_select(_ptr(conf), _ptr(draft_len), n, k_max, _ptr(cost), cost.numel(),
                                  int(t_base), int(n_bonus), _ptr(kept), _ptr(budget),
-                                 _ptr(survival), _ptr(dev_error), None, 0, _stream(stream)),
+                                 _ptr(survival), _ptr(dev_error), _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream(stream)),
            "sv_budget_select")
 
 
@@ -245,7 +249,9 @@ def budget_select(conf, draft_len, cost, t_base, n_bonus, stream=None):
     budget = torch.empty(1, dtype=torch.int32, device=dev)
     survival = torch.empty(n, k_max, dtype=torch.float32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survival, err, stream)
+    ws = torch.empty(max(1, sv_budget_workspace_bytes(n, k_max)), dtype=torch.uint8, device=dev)
+    sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survival, err, stream,
+                     ws=ws)
     return dict(kept=kept, budget=budget, survival=survival, dev_error=err)
 
 

@@ -34,9 +34,10 @@ const char* sv_status_str(sv_status s) {
 }
 
 size_t sv_budget_workspace_bytes(int32_t n_req, int32_t k_max) {
-    (void)n_req;
-    (void)k_max;
-    return 0;
+    if (n_req < 0 || k_max < 0 || n_req > SV_MAX_BUDGET_SLOTS || k_max > SV_MAX_DRAFT ||
+        (int64_t)n_req * k_max > SV_MAX_BUDGET_SLOTS)
+        return 0;
+    return sv::budget_workspace_bytes(n_req, k_max);
 }
 
 size_t sv_verify_workspace_bytes(int32_t n_req, int32_t k_max) {
@@ -70,18 +71,19 @@ sv_status sv_budget_select(const float* conf, const int32_t* draft_len, int32_t 
                            int32_t k_max, const float* cost, int32_t cost_len, int32_t t_base,
                            int32_t n_bonus, int32_t* kept, int32_t* budget, float* survival,
                            int32_t* dev_error, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (n_req < 0 || k_max < 0) return SV_ERR_SHAPE;
     if (cost == nullptr || budget == nullptr) return SV_ERR_NULL;
     if (n_req > 0 && (draft_len == nullptr || kept == nullptr)) return SV_ERR_NULL;
     if (n_req > 0 && k_max > 0 && conf == nullptr) return SV_ERR_NULL;
-    if (n_req > SV_MAX_BUDGET_SLOTS || (int64_t)n_req * k_max > SV_MAX_BUDGET_SLOTS)
+    if (n_req > SV_MAX_BUDGET_SLOTS || k_max > SV_MAX_DRAFT ||
+        (int64_t)n_req * k_max > SV_MAX_BUDGET_SLOTS)
         return SV_ERR_SHAPE;
     if (t_base < 0 || n_bonus < 0) return SV_ERR_VALUE;
     if ((int64_t)cost_len < (int64_t)t_base + (int64_t)n_req * k_max + 1) return SV_ERR_SHAPE;
+    const size_t need = sv::budget_workspace_bytes(n_req, k_max);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return SV_ERR_WORKSPACE;
     return launched(sv::launch_budget(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept,
-                                      budget, survival, dev_error, as_stream(stream)));
+                                      budget, survival, dev_error, ws, as_stream(stream)));
 }
 
 sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,

@@ -1,40 +1,47 @@
-// Adaptive verification budget on one workgroup (gfx950).
+// Adaptive verification budget (gfx950).
 //
 // FOS blog "추측 디코딩과 vLLM 적응형 검증", section "적응형 검증 > 동작",
 // steps 1-3; agentlens "vLLM DSpark을 활용한 적응형 검증(Adaptive
 // Verification)", section "DSpark 신뢰도 스케줄링 메커니즘" (Global Top-B
 // Selection, Budget Calculation).
 //
-// At most SV_MAX_BUDGET_SLOTS draft slots, so the whole problem lives on one
-// CU:
-//   0. every global input is requested up front (confidences, draft lengths,
-//      and the cost entries of this thread's ranks) so their latencies
-//      overlap;
-//   1. one thread per request forms the survival products in position order
-//      (fp32 round-to-nearest, no contraction) and writes that request's
-//      keys — (bits that fall as survival rises) << 32 | slot id, unique —
-//      as one ascending run: survival never rises with position, so every
-//      request's run is already sorted;
-//   2. a merge tree joins the runs pairwise, ceil(log2 n) levels, two LDS
-//      buffers in turn: each key lands at (its index in its run) + (number of
-//      keys below it in the partner run), found by one binary search — exact
-//      and order free because keys are unique.  The order is survival
-//      descending, then request, then position;
-//   3. fixed-point prefix sums sum floor(s * 2^40) in uint64 (exact, order
-//      free), fp64 scores (n_bonus + S * 2^-40) / cost[t_base + B], and the
-//      first maximiser;
-//   4. kept counts by integer LDS atomics over the first B ranks.
+// Every draft slot gets a unique 64-bit key, (bits that fall as survival
+// rises) << 32 | slot id, so that ascending keys are the global order —
+// survival descending, then request, then position.  A slot's place in that
+// order is the number of keys below its own, which the GPU counts in
+// parallel instead of sorting:
+//
+//   rank kernel — one 1024-thread workgroup per 16 query slots.  Each
+//     workgroup stages every confidence in LDS with coalesced loads, forms
+//     every survival product (one thread per request, position order, fp32
+//     round-to-nearest, no contraction — identical bits in every
+//     workgroup) and keeps the keys in LDS.  Each wave then ranks one query
+//     slot: every lane holds one key of each 64-key chunk of the batch, one
+//     compare per chunk, and the population count of the ballot adds 64
+//     comparisons at once.  It writes each query's rank and places its
+//     survival at that rank in the workspace.
+//   finish kernel — one workgroup (DPP wave scans): the fixed-point prefix sums
+//     sum floor(s * 2^40) over the rank-ordered survivals (exact uint64,
+//     order free), the fp64 scores (n_bonus + S * 2^-40) / cost[t_base + B],
+//     the first maximiser B and the kept counts #{j : rank(r, j) < B}.
+//
+// Workspace: [0] total real slots (int32), then ranks [n_slots] int32 and the
+// rank-ordered survivals [n_slots] fp32.  Every word the finish kernel reads
+// is written by the rank kernel of the same call, so it needs no clearing.
 #include "sv_device.h"
 #include "sv_launch.h"
 
 namespace sv {
 namespace {
 
-constexpr int kBudgetThreads = 1024;
-constexpr int kBudgetWaves = kBudgetThreads / kWave;
-// Keys of slots past a request's draft length: above every real key (whose
-// high word is at most 0x7fffffff), unique through the slot id.
-constexpr uint64_t kPadKey = 0x8000000000000000ull;
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;                        // 16
+constexpr int kQueries = kWaves;                                // query slots per rank workgroup
+// conf rows padded to an odd stride: n_req * (k_max | 1) floats, largest at
+// k_max = 2 (4096 requests x 3)
+constexpr int kConfLds = SV_MAX_BUDGET_SLOTS + SV_MAX_BUDGET_SLOTS / 2;
+constexpr int kPerThread = SV_MAX_BUDGET_SLOTS / kThreads;      // 8
+constexpr size_t kHeaderBytes = 16;
 
 __device__ __forceinline__ float clamp_confidence(float c) {
     // NaN, negatives and -0 -> +0; above 1 -> 1.
@@ -42,7 +49,7 @@ __device__ __forceinline__ float clamp_confidence(float c) {
     return c > 1.0f ? 1.0f : c;
 }
 
-// Survival s in [0, 1] -> high key word that grows as s falls (s >= +0).
+// Survival s in [0, 1] -> key whose high word grows as s falls.
 __device__ __forceinline__ uint64_t survival_key(float s, int slot) {
     return ((uint64_t)(0x7fffffffu - __float_as_uint(s)) << 32) | (uint32_t)slot;
 }
@@ -51,253 +58,281 @@ __device__ __forceinline__ float key_survival(uint64_t key) {
     return __uint_as_float(0x7fffffffu - (uint32_t)(key >> 32));
 }
 
-// Number of keys in seg[0 .. len) below `key` (seg ascending, keys unique).
-__device__ __forceinline__ int lower_bound(const uint64_t* seg, int len, uint64_t key) {
-    int lo = 0;
-    while (len > 0) {
-        const int half = len >> 1;
-        if (seg[lo + half] < key) {
-            lo += half + 1;
-            len -= half + 1;
-        } else {
-            len = half;
-        }
-    }
-    return lo;
+constexpr uint64_t kNoSlot = ~0ull;  // past draft_len: after every real key
+
+__device__ __forceinline__ int clamp_len(int K, int k_max) { return K < 0 ? 0 : (K > k_max ? k_max : K); }
+
+struct BudgetWs {
+    int32_t* total;
+    int32_t* rank;
+    float* sorted;
+};
+
+__device__ __forceinline__ BudgetWs budget_ws(void* ws, int n_slots) {
+    char* base = static_cast<char*>(ws);
+    BudgetWs w;
+    w.total = reinterpret_cast<int32_t*>(base);
+    w.rank = reinterpret_cast<int32_t*>(base + kHeaderBytes);
+    w.sorted = reinterpret_cast<float*>(base + kHeaderBytes + (size_t)n_slots * sizeof(int32_t));
+    return w;
 }
 
-// Block-wide exclusive scan of one uint64 per thread.
-__device__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* wave_tot) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const uint64_t incl = wave_incl_scan<uint64_t>(v, lane);
-    if (lane == kWave - 1) wave_tot[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-        uint64_t t = lane < kBudgetWaves ? wave_tot[lane] : 0ull;
-        t = wave_incl_scan<uint64_t>(t, lane);
-        if (lane < kBudgetWaves) wave_tot[lane] = t;
-    }
-    __syncthreads();
-    return (wave == 0 ? 0ull : wave_tot[wave - 1]) + incl - v;
-}
-
-// E = ranks per thread (contiguous), n_req * k_max <= 1024 * E.
-template <int E>
-__global__ __launch_bounds__(kBudgetThreads) void budget_kernel(
+__global__ __launch_bounds__(kThreads) void rank_kernel(
     const float* __restrict__ conf, const int32_t* __restrict__ draft_len, int n_req, int k_max,
-    const float* __restrict__ cost, int t_base, int n_bonus, int32_t* __restrict__ kept,
-    int32_t* __restrict__ budget, float* __restrict__ survival, int32_t* dev_error) {
-    __shared__ uint64_t buf[2][SV_MAX_BUDGET_SLOTS];
-    __shared__ uint64_t wave_tot[kBudgetWaves];
-    __shared__ double best_score_s[kBudgetWaves];
-    __shared__ int32_t best_b_s[kBudgetWaves];
-    __shared__ int32_t total_slots_s, err_s;
+    float* __restrict__ survival, int32_t* dev_error, void* ws) {
+    // confidences at r * kp + j with an odd row stride kp (conflict-free LDS
+    // reads when lanes walk consecutive requests); keys transposed, j * n_req + r
+    __shared__ float conf_s[kConfLds];
+    __shared__ uint64_t keys[SV_MAX_BUDGET_SLOTS];
+    __shared__ int32_t total_s, err_s;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int n_slots = n_req * k_max;
-    const int first_rank = tid * E;
-    float* conf_s = reinterpret_cast<float*>(buf[1]);  // staging, dead before buf[1] is used
+    const int kp = k_max | 1;
+    const bool lead = blockIdx.x == 0;  // writes survival, total and the error bits
+    const BudgetWs w = budget_ws(ws, n_slots);
 
-    // 0. requests for every global input this thread will need
-    float cst[E];
+    // every global input requested at once: confidences (coalesced) and the
+    // draft lengths of the requests this thread will chain
+    float c[kPerThread];
+    int32_t dl[kPerThread];
 #pragma unroll
-    for (int q = 0; q < E; ++q) {
-        const int rank = first_rank + q;
-        cst[q] = rank < n_slots ? cost[t_base + rank + 1] : 1.0f;
+    for (int q = 0; q < kPerThread; ++q) {
+        const int x = tid + q * kThreads;
+        c[q] = x < n_slots ? conf[x] : 0.0f;
+        dl[q] = x < n_req ? draft_len[x] : 0;
     }
-    const float cost0 = cost[t_base];
-    constexpr int kMaxReqPerThread = SV_MAX_BUDGET_SLOTS / kBudgetThreads;
-    int dl[kMaxReqPerThread];
-#pragma unroll
-    for (int i = 0; i < kMaxReqPerThread; ++i) {
-        const int r = tid + i * kBudgetThreads;
-        dl[i] = r < n_req ? draft_len[r] : 0;
-    }
-    for (int i = tid; i < n_slots; i += kBudgetThreads) conf_s[i] = conf[i];
     if (tid == 0) {
-        total_slots_s = 0;
+        total_s = 0;
         err_s = 0;
     }
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int x = tid + q * kThreads;
+        if (x < n_slots) {
+            const int r = x / k_max;
+            conf_s[r * kp + (x - r * k_max)] = clamp_confidence(c[q]);
+        }
+    }
     __syncthreads();
 
-    // 1. survival products and the per-request sorted runs of keys (buf[0])
-    int my_err = 0, my_total = 0;
+    // survival products, one thread per request
+    int my_total = 0, my_err = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxReqPerThread; ++i) {
-        const int r = tid + i * kBudgetThreads;
-        if (r >= n_req) break;
-        int K = dl[i];
-        if (K < 0 || K > k_max) {
-            my_err |= SV_DEV_BAD_DRAFT_LEN;
-            K = K < 0 ? 0 : k_max;
-        }
-        my_total += K;
-        float s = 1.0f;
-        for (int j = 0; j < k_max; ++j) {
-            const int slot = r * k_max + j;
-            if (j < K) {
-                s = __fmul_rn(s, clamp_confidence(conf_s[slot]));
-                buf[0][slot] = survival_key(s, slot);
-                if (survival != nullptr) survival[slot] = s;
-            } else {
-                buf[0][slot] = kPadKey | (uint32_t)slot;
-                if (survival != nullptr) survival[slot] = 0.0f;
+    for (int q = 0; q < kPerThread; ++q) {
+        const int r = tid + q * kThreads;
+        if (r < n_req) {
+            const int K = clamp_len(dl[q], k_max);
+            if (K != dl[q]) my_err |= SV_DEV_BAD_DRAFT_LEN;
+            my_total += K;
+            float s = 1.0f;
+            for (int j = 0; j < k_max; ++j) {
+                const int slot = r * k_max + j;
+                if (j < K) s = __fmul_rn(s, conf_s[r * kp + j]);
+                keys[j * n_req + r] = j < K ? survival_key(s, slot) : kNoSlot;
             }
         }
     }
-    if (my_total) atomicAdd(&total_slots_s, my_total);
-    // cost entries are checked here so their loads complete under this phase
-    int cost_bad = 0;
-#pragma unroll
-    for (int q = 0; q < E; ++q) cost_bad |= (cst[q] > 0.0f && is_finite_bits(cst[q])) ? 0 : 1 << q;
-    const bool cost0_bad = !(cost0 > 0.0f && is_finite_bits(cost0));
-    if (my_err) atomicOr(&err_s, my_err);
+    if (lead) {
+        if (my_total) atomicAdd(&total_s, my_total);
+        if (my_err) atomicOr(&err_s, my_err);
+    }
     __syncthreads();
-
-    // 2. merge tree over runs of k_max << level slots
-    int src = 0;
-    for (int run = k_max; run < n_slots; run <<= 1) {
-        const uint64_t* in = buf[src];
-        uint64_t* out = buf[src ^ 1];
+    if (lead) {
+        // after the last barrier, so that no barrier waits for these stores
+        if (tid == 0) {
+            w.total[0] = total_s;
+            raise_error(dev_error, err_s);
+        }
+        if (survival != nullptr) {
 #pragma unroll
-        for (int q = 0; q < E; ++q) {
-            const int p = first_rank + q;
-            if (p < n_slots) {
-                const uint64_t key = in[p];
-                const int r_idx = p / run;
-                const int pair_base = (r_idx & ~1) * run;
-                const int partner = (r_idx ^ 1) * run;
-                int pos = p - pair_base;  // own index in run, plus left run if right
-                if (partner < n_slots) {
-                    const int plen = min(run, n_slots - partner);
-                    pos = (p - r_idx * run) + lower_bound(in + partner, plen, key);
+            for (int q = 0; q < kPerThread; ++q) {
+                const int x = tid + q * kThreads;
+                if (x < n_slots) {
+                    const int r = x / k_max;
+                    const uint64_t key = keys[(x - r * k_max) * n_req + r];
+                    survival[x] = key != kNoSlot ? key_survival(key) : 0.0f;
                 }
-                out[pair_base + pos] = key;
             }
         }
-        src ^= 1;
-        __syncthreads();
     }
-    const uint64_t* sorted = buf[src];
-    int32_t* kept_s = reinterpret_cast<int32_t*>(buf[src ^ 1]);
-    for (int r = tid; r < n_req; r += kBudgetThreads) kept_s[r] = 0;
 
-    // 3. fixed-point prefix sums over ranks, scores, first maximiser
-    const int total = total_slots_s;
-    uint64_t fx[E];
+    // wave `wave` ranks one query slot: every lane holds one key of each
+    // 64-key chunk, one compare per chunk, and the population count of the
+    // ballot adds 64 comparisons at once (the key order in LDS is irrelevant)
+    const int x = blockIdx.x * kQueries + wave;
+    if (x >= n_slots) return;  // wave-uniform; no barrier follows
+    const int xr = x / k_max;
+    const uint64_t v = keys[(x - xr * k_max) * n_req + xr];  // same address in every lane
+    const uint64_t qk = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                        __builtin_amdgcn_readfirstlane((uint32_t)v);
+    int cnt = 0;
+    int base = 0;
+    for (; base + 4 * kWave <= n_slots; base += 4 * kWave) {
+        uint64_t ref[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ref[u] = keys[base + u * kWave + lane];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cnt += __popcll(__ballot(ref[u] < qk));
+    }
+    for (; base < n_slots; base += kWave) {
+        const int i = base + lane;
+        const uint64_t ref = i < n_slots ? keys[i] : kNoSlot;
+        cnt += __popcll(__ballot(ref < qk));
+    }
+    if (lane == 0) {
+        w.rank[x] = cnt;
+        if (qk != kNoSlot) w.sorted[cnt] = key_survival(qk);
+    }
+}
+
+// (score, B) pair; the better one has the larger score, then the smaller B.
+struct Cand {
+    double score;
+    int32_t b;
+    int32_t pad;
+};
+
+struct BetterOp {
+    __device__ __forceinline__ Cand operator()(Cand a, Cand c) const {
+        return (c.score > a.score || (c.score == a.score && c.b < a.b)) ? c : a;
+    }
+};
+
+__global__ __launch_bounds__(kThreads) void finish_kernel(
+    int n_req, int k_max, const float* __restrict__ cost, int t_base, int n_bonus,
+    int32_t* __restrict__ kept, int32_t* __restrict__ budget, int32_t* dev_error, void* ws) {
+    __shared__ uint8_t in_budget[SV_MAX_BUDGET_SLOTS];
+    __shared__ uint64_t wave_tot[kWaves];
+    __shared__ Cand wave_best[kWaves];
+    __shared__ int32_t best_b_s;
+    __shared__ int32_t err_s;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int n_slots = n_req * k_max;
+    const BudgetWs w = budget_ws(ws, n_slots);
+    // this thread's ranks: [first, first + per), per = ceil(n_slots / 1024)
+    const int per = (n_slots + kThreads - 1) / kThreads;
+    const int first = tid * per;
+
+    // every load first: rank-ordered survivals and cost entries of this
+    // thread's ranks, the ranks of slots tid + 1024 q, the total
+    float srt[kPerThread], cst[kPerThread];
+    int32_t rk[kPerThread];
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        srt[q] = 0.0f;
+        cst[q] = 1.0f;
+        rk[q] = 0;
+        if (q >= per) continue;  // uniform: per = ceil(n_slots / 1024)
+        const int rank = first + q;
+        if (rank < n_slots) {
+            srt[q] = w.sorted[rank];
+            cst[q] = cost[t_base + rank + 1];
+        }
+        const int x = tid + q * kThreads;
+        if (x < n_slots) rk[q] = w.rank[x];
+    }
+    const float cost0 = cost[t_base];
+    const int total = n_slots > 0 ? w.total[0] : 0;
+    if (tid == 0) err_s = 0;
+
+    uint64_t fx[kPerThread];
     uint64_t local = 0;
 #pragma unroll
-    for (int q = 0; q < E; ++q) {
-        fx[q] = 0;
-        if (first_rank + q < total) fx[q] = (uint64_t)(key_survival(sorted[first_rank + q]) * 0x1p40f);
-        local += fx[q];  // exact scaling; truncation = floor
+    for (int q = 0; q < kPerThread; ++q) {
+        // s * 2^40 is exact in fp32; the conversion truncates = floor
+        fx[q] = (q < per && first + q < total) ? (uint64_t)(srt[q] * 0x1p40f) : 0ull;
+        local += fx[q];
     }
-    uint64_t run_sum = block_excl_scan_u64(local, wave_tot);
+    // block exclusive scan: DPP wave scan, then the totals of earlier waves
+    const uint64_t incl = wave_incl_sum_dpp<uint64_t>(local, lane);
+    if (lane == kWave - 1) wave_tot[wave] = incl;
+    __syncthreads();
+    uint64_t run_sum = incl - local;
+    for (int v = 0; v < wave; ++v) run_sum += wave_tot[v];
 
-    double best = -__builtin_inf();
-    int best_b = 0x7fffffff;
+    Cand best{-__builtin_inf(), 0x7fffffff, 0};
     int cost_err = 0;
     if (tid == 0) {  // B = 0
-        if (!cost0_bad)
-            best = (double)n_bonus / (double)cost0;
+        if (cost0 > 0.0f && is_finite_bits(cost0))
+            best.score = (double)n_bonus / (double)cost0;
         else
             cost_err = SV_DEV_BAD_COST;
-        best_b = 0;
+        best.b = 0;
     }
 #pragma unroll
-    for (int q = 0; q < E; ++q) {
-        const int rank = first_rank + q;
+    for (int q = 0; q < kPerThread; ++q) {
+        if (q >= per) break;  // uniform
+        const int rank = first + q;
         if (rank < total) {
             run_sum += fx[q];
-            const int b = rank + 1;
-            double sc = -__builtin_inf();
-            if (!((cost_bad >> q) & 1)) {
-                sc = __dadd_rn((double)n_bonus, __dmul_rn((double)run_sum, 0x1p-40));
-                sc = __ddiv_rn(sc, (double)cst[q]);
+            if (cst[q] > 0.0f && is_finite_bits(cst[q])) {
+                // run_sum < 2^53 and 2^-40 is a power of two: the product is exact
+                const double sc = ((double)n_bonus + (double)run_sum * 0x1p-40) / (double)cst[q];
+                best = BetterOp{}(best, Cand{sc, rank + 1, 0});
             } else {
                 cost_err = SV_DEV_BAD_COST;
             }
-            if (sc > best || (sc == best && b < best_b)) {
-                best = sc;
-                best_b = b;
-            }
         }
     }
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const double ob = __shfl_xor(best, o);
-        const int obb = __shfl_xor(best_b, o);
-        if (ob > best || (ob == best && obb < best_b)) {
-            best = ob;
-            best_b = obb;
-        }
-    }
+    best = lane63(wave_scan_dpp(best, lane, BetterOp{}));
     if (cost_err) atomicOr(&err_s, cost_err);
-    if (lane == 0) {
-        best_score_s[wave] = best;
-        best_b_s[wave] = best_b;
-    }
+    if (lane == 0) wave_best[wave] = best;
     __syncthreads();
     if (wave == 0) {
-        best = lane < kBudgetWaves ? best_score_s[lane] : -__builtin_inf();
-        best_b = lane < kBudgetWaves ? best_b_s[lane] : 0x7fffffff;
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            const double ob = __shfl_xor(best, o);
-            const int obb = __shfl_xor(best_b, o);
-            if (ob > best || (ob == best && obb < best_b)) {
-                best = ob;
-                best_b = obb;
-            }
-        }
-        if (lane == 0) best_b_s[0] = best_b;
+        Cand c = lane < kWaves ? wave_best[lane] : Cand{-__builtin_inf(), 0x7fffffff, 0};
+        c = lane63(wave_scan_dpp(c, lane, BetterOp{}));
+        if (lane == 0) best_b_s = c.b;
     }
     __syncthreads();
-    const int B = best_b_s[0];
+    const int B = best_b_s;
 
-    // 4. kept counts
+    // kept counts: a request's slots ranked before B (slots past draft_len
+    // rank at `total` or later, never before B)
 #pragma unroll
-    for (int q = 0; q < E; ++q)
-        if (first_rank + q < B) atomicAdd(&kept_s[(int)(uint32_t)sorted[first_rank + q] / k_max], 1);
+    for (int q = 0; q < kPerThread; ++q) {
+        if (q >= per) break;  // uniform
+        const int x = tid + q * kThreads;
+        if (x < n_slots) in_budget[x] = rk[q] < B ? 1 : 0;
+    }
     __syncthreads();
-    for (int r = tid; r < n_req; r += kBudgetThreads) kept[r] = kept_s[r];
+    for (int r = tid; r < n_req; r += kThreads) {
+        int k_in = 0;
+        for (int j = 0; j < k_max; ++j) k_in += in_budget[r * k_max + j];
+        kept[r] = k_in;
+    }
     if (tid == 0) {
         budget[0] = B;
         raise_error(dev_error, err_s);
     }
 }
 
-template <int E>
-void launch_e(const float* conf, const int32_t* draft_len, int n_req, int k_max,
-              const float* cost, int t_base, int n_bonus, int32_t* kept, int32_t* budget,
-              float* survival, int32_t* dev_error, hipStream_t stream) {
-    hipLaunchKernelGGL(budget_kernel<E>, dim3(1), dim3(kBudgetThreads), 0, stream, conf,
-                       draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
-                       dev_error);
-}
-
 }  // namespace
+
+size_t budget_workspace_bytes(int n_req, int k_max) {
+    if (n_req <= 0 || k_max < 0) return 0;
+    return kHeaderBytes + (size_t)n_req * (size_t)k_max * (sizeof(int32_t) + sizeof(float));
+}
 
 hipError_t launch_budget(const float* conf, const int32_t* draft_len, int n_req, int k_max,
                          const float* cost, int t_base, int n_bonus, int32_t* kept,
-                         int32_t* budget, float* survival, int32_t* dev_error,
+                         int32_t* budget, float* survival, int32_t* dev_error, void* ws,
                          hipStream_t stream) {
     const int n_slots = n_req * k_max;
-    if (n_slots <= kBudgetThreads)
-        launch_e<1>(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
-                    dev_error, stream);
-    else if (n_slots <= 2 * kBudgetThreads)
-        launch_e<2>(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
-                    dev_error, stream);
-    else if (n_slots <= 4 * kBudgetThreads)
-        launch_e<4>(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
-                    dev_error, stream);
-    else
-        launch_e<8>(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept, budget, survival,
-                    dev_error, stream);
+    if (n_req > 0) {
+        const unsigned blocks = (unsigned)(n_slots > 0 ? (n_slots + kQueries - 1) / kQueries : 1);
+        hipLaunchKernelGGL(rank_kernel, dim3(blocks), dim3(kThreads), 0, stream, conf, draft_len,
+                           n_req, k_max, survival, dev_error, ws);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kThreads), 0, stream, n_req, k_max, cost,
+                       t_base, n_bonus, kept, budget, dev_error, ws);
     return hipGetLastError();
 }
 

@@ -85,6 +85,80 @@ __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
     return v;
 }
 
+// ------------------------------------------------------------ DPP lane moves
+// Cross-lane moves through the VALU's data-parallel-primitive path (a few
+// cycles) instead of LDS permutes.  gfx9 DPP controls: row_shr:n = 0x110 + n
+// (lane i of each 16-lane row reads lane i - n of that row), row_bcast:15 =
+// 0x142 (lane 15 of each row feeds the next row), row_bcast:31 = 0x143
+// (lane 31 feeds rows 2 and 3).  Lanes whose source is outside the row, or
+// whose row is masked off, read 0; every caller below ignores those lanes.
+// All 64 lanes must be active.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <int CTRL, int ROW_MASK, typename T>
+__device__ __forceinline__ T dpp_move_t(T v) {
+    static_assert(sizeof(T) % 4 == 0, "32-bit words");
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) w[i] = dpp_move<CTRL, ROW_MASK>(w[i]);
+    T r;
+    __builtin_memcpy(&r, w, sizeof(T));
+    return r;
+}
+
+// Value of lane 63, in every lane.
+template <typename T>
+__device__ __forceinline__ T lane63(T v) {
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) w[i] = __builtin_amdgcn_readlane(w[i], 63);
+    T r;
+    __builtin_memcpy(&r, w, sizeof(T));
+    return r;
+}
+
+// Inclusive scan over the 64 lanes, op(earlier, later) associative; a fixed
+// combination order (deterministic).  Lane 63 ends with the whole-wave value.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_scan_dpp(T v, int lane, Op op) {
+    const int rl = lane & 15;
+    T t;
+    t = dpp_move_t<0x111, 0xf>(v);
+    if (rl >= 1) v = op(t, v);
+    t = dpp_move_t<0x112, 0xf>(v);
+    if (rl >= 2) v = op(t, v);
+    t = dpp_move_t<0x114, 0xf>(v);
+    if (rl >= 4) v = op(t, v);
+    t = dpp_move_t<0x118, 0xf>(v);
+    if (rl >= 8) v = op(t, v);
+    t = dpp_move_t<0x142, 0xa>(v);
+    if (lane & 16) v = op(t, v);
+    t = dpp_move_t<0x143, 0xc>(v);
+    if (lane & 32) v = op(t, v);
+    return v;
+}
+
+struct AddOp {
+    template <typename T>
+    __device__ __forceinline__ T operator()(T a, T b) const { return a + b; }
+};
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_sum_dpp(T v, int lane) {
+    return wave_scan_dpp(v, lane, AddOp{});
+}
+
+// Whole-wave sum, in every lane.
+template <typename T>
+__device__ __forceinline__ T wave_sum_dpp(T v, int lane) {
+    return lane63(wave_scan_dpp(v, lane, AddOp{}));
+}
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
 // Easy as 1, 2, 3", SC'11, section 3): per round the products of the two
 // multipliers with counter words 0 and 2 are split in high and low halves,

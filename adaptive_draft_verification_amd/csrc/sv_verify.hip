@@ -8,16 +8,18 @@
 // from the normalised residual max(0, p - q)), and section "평균 수락 길이"
 // (the bonus token).
 //
-// Pass 1, one 256-thread workgroup per candidate row: target rows 0..b and
+// Pass 1, one 512-thread workgroup per candidate row: target rows 0..b and
 // (stochastic) draft rows 0..b-1 of each request.  The grid is the host-known
 // capacity; workgroups of rows past a request's kept count do nothing.  The
 // grid runs position-major from the last draft position down to position 0,
 // so the rows pass 2 most often reads again (the first rejections happen
 // early) are the last ones streamed and are still in the Infinity Cache.
 //
-// Row statistics.  The row is streamed once with 16-byte loads.  Stochastic
-// rows keep, per thread, an offset taken from the max of the thread's first
-// 16-byte chunk and accumulate exp2(z * log2(e)/T - offset) in independent
+// Row statistics.  The row is streamed once with 16-byte non-temporal loads
+// (each byte is read once; keeping it out of the caches measurably raises
+// the streaming rate).  Stochastic rows keep, per thread, an offset taken
+// from the max of the thread's first 16-byte chunk and accumulate
+// exp2(z * log2(e)/T - offset) in independent
 // fp32 partial sums, so the hot loop has no per-element max; per-thread
 // (offset, sum) pairs merge by rescaling in a fixed tree.  If that shortcut
 // overflows (a later logit more than ~88/T above the first chunk's max) the
@@ -28,24 +30,53 @@
 // Pass 2, one 1024-thread workgroup per request.  Wave 0 draws the Philox
 // uniforms of the kept positions, tests u < 2^(log2 p(d) - log2 q(d)) (greedy:
 // d == argmax) and takes the first rejection with a ballot.  The token at L
-// is drawn by inverse CDF over the residual row (or the bonus row): one sweep
-// sums weights per 8192-id tile (one wave reduction per tile, no barriers,
-// several tiles in flight), a wave scan over tile sums finds the tile holding
-// v * W, and only that tile is read again, with a block-wide exclusive scan.
+// is drawn by inverse CDF over the residual row (or the bonus row): waves
+// claim 2048-id super-groups from an LDS counter and stream them (the next
+// one's loads in flight while the current one is summed, no barrier in the
+// stream), each super-group's sum goes to LDS, and wave 0 walks the sums in
+// id order and reads only the crossing super-group again.
 #include "sv_device.h"
 #include "sv_launch.h"
 
 namespace sv {
 namespace {
 
-constexpr int kThreads = 256;                        // pass 1 workgroup
-constexpr int kUnroll = 4;                           // pass 1: 16-byte loads in flight per thread
+// Launch shapes (overridable at build time for tuning sweeps).  Measured on
+// MI355X, 256 requests x 8 rows x 129280 bf16: non-temporal pass-1 loads move
+// the stream from ~5.8 to ~6.8 TB/s; 512-thread rows edge out 256 and 1024.
+#ifndef SV_PASS1_THREADS
+#define SV_PASS1_THREADS 512
+#endif
+#ifndef SV_PASS1_UNROLL
+#define SV_PASS1_UNROLL 4
+#endif
+#ifndef SV_PASS1_NONTEMPORAL
+#define SV_PASS1_NONTEMPORAL 1
+#endif
+#ifndef SV_DRAW_UNROLL
+#define SV_DRAW_UNROLL 4
+#endif
+constexpr int kThreads = SV_PASS1_THREADS;           // pass 1 workgroup
+constexpr int kUnroll = SV_PASS1_UNROLL;             // pass 1: 16-byte loads in flight per thread
 constexpr int kP2Threads = 1024;                     // pass 2 workgroup (stochastic)
 constexpr int kP2Waves = kP2Threads / kWave;
-constexpr int kTile = kP2Threads * 8;                // ids per tile of the draw
-constexpr int kMaxTiles = SV_MAX_VOCAB / kTile;      // 128
-constexpr int kTilesPerLane = kMaxTiles / kWave;     // tile scan: 2 tiles per lane of one wave
-constexpr int kDrawUnroll = 4;                       // tiles in flight per thread in the sweep
+constexpr int kDrawUnroll = SV_DRAW_UNROLL;          // 8-id groups per lane per super-group
+
+// One 16-byte load of streamed row data (optionally non-temporal: read once,
+// no point keeping it in the caches).
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p) {
+    static_assert(sizeof(T) == 16, "16-byte loads only");
+#if SV_PASS1_NONTEMPORAL
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    T out;
+    __builtin_memcpy(&out, &v, 16);
+    return out;
+#else
+    return *p;
+#endif
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kInf = __builtin_inff();
 
@@ -144,7 +175,7 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
     int i = tid;
     if (i < nvec) {
         float x[E];
-        V::unpack(vrow[i], x);
+        V::unpack(stream_load(vrow + i), x);
         float m = x[0];
 #pragma unroll
         for (int k = 1; k < E; ++k) m = fmaxf(m, x[k]);
@@ -162,7 +193,7 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
     for (; i + (kUnroll - 1) * kThreads < nvec; i += kUnroll * kThreads) {
         raw_t w[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) w[u] = vrow[i + u * kThreads];
+        for (int u = 0; u < kUnroll; ++u) w[u] = stream_load(vrow + i + u * kThreads);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             float x[E];
@@ -173,7 +204,7 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
     }
     for (; i < nvec; i += kThreads) {
         float x[E];
-        V::unpack(vrow[i], x);
+        V::unpack(stream_load(vrow + i), x);
 #pragma unroll
         for (int k = 0; k < E; ++k) acc[k] += fast_exp2(fmaf(x[k], c, -a_t));
     }
@@ -225,7 +256,7 @@ __device__ void row_argmax(const char* row, int vocab, float* redf, int* redi, f
     for (; i + (kUnroll - 1) * kThreads < nvec; i += kUnroll * kThreads) {
         raw_t w[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) w[u] = vrow[i + u * kThreads];
+        for (int u = 0; u < kUnroll; ++u) w[u] = stream_load(vrow + i + u * kThreads);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             float x[E];
@@ -249,7 +280,7 @@ __device__ void row_argmax(const char* row, int vocab, float* redf, int* redi, f
     }
     for (; i < nvec; i += kThreads) {
         float x[E];
-        V::unpack(vrow[i], x);
+        V::unpack(stream_load(vrow + i), x);
 #pragma unroll
         for (int k = 0; k < E; ++k) {
             nan |= x[k] != x[k];
@@ -372,15 +403,26 @@ __device__ __forceinline__ void weights_from(const float* zp, const float* zq, f
     }
 }
 
+// Draw geometry: a super-group is Geom<DT>::kIds consecutive ids, one wave's
+// unit of work in the sweep (lane l takes the 8-id groups at 8 l + 512 u,
+// u < U; fp32 rows take half as many groups per lane: twice the registers).
+template <sv_dtype DT>
+struct Geom {
+    static constexpr int kU = DT == SV_BF16 ? kDrawUnroll : (kDrawUnroll + 1) / 2;
+    static constexpr int kIds = kWave * 8 * kU;
+    static constexpr int kMaxGroups = (SV_MAX_VOCAB + kIds - 1) / kIds;
+    static constexpr int kGroupsPerLane = (kMaxGroups + kWave - 1) / kWave;
+    static constexpr int kIdsPerLane = kIds / kWave;  // second look: one lane's ids
+};
+constexpr int kMaxGroupsAny = Geom<SV_F32>::kMaxGroups > Geom<SV_BF16>::kMaxGroups
+                                  ? Geom<SV_F32>::kMaxGroups
+                                  : Geom<SV_BF16>::kMaxGroups;
+
 struct DrawSmem {
-    float wsum[kMaxTiles * kP2Waves];  // per tile, per wave partial sums
-    float wtot[kP2Waves];
-    int cand;
-    int lastpos;
-    int tile;
-    float base;
-    float target;
-    float total;
+    float gsum[kMaxGroupsAny];  // per super-group weight sums
+    int next;                // next unclaimed super-group
+    int tok;                 // the drawn id
+    float total;             // W
 };
 
 // Per-thread sum of 8 weights, in id order.
@@ -391,152 +433,213 @@ __device__ __forceinline__ float sum8(const float* w) {
     return s;
 }
 
+struct DrawRow {
+    const char* prow;
+    const char* qrow;
+    int vocab;
+    bool aligned;  // both rows 16-byte aligned
+    float c, ap, isp, aq, isq;
+};
+
+// A super-group's raw words for one lane: U 8-id groups of each row.
+template <sv_dtype DT, bool RESID>
+struct GroupRaw {
+    Raw8<DT> p[Geom<DT>::kU], q[Geom<DT>::kU];
+};
+
+// True if super-group g lies wholly inside the row and both rows are aligned.
+template <sv_dtype DT>
+__device__ __forceinline__ bool group_fast(const DrawRow& d, int g) {
+    return d.aligned && (g + 1) * Geom<DT>::kIds <= (d.vocab & ~7);
+}
+
+template <sv_dtype DT, bool RESID>
+__device__ __forceinline__ void group_fetch(const DrawRow& d, int g, int lane,
+                                            GroupRaw<DT, RESID>& r) {
+    const int e = g * Geom<DT>::kIds + lane * 8;
+#pragma unroll
+    for (int u = 0; u < Geom<DT>::kU; ++u) {
+        r.p[u].fetch(d.prow, e + u * kWave * 8);
+        if (RESID) r.q[u].fetch(d.qrow, e + u * kWave * 8);
+    }
+}
+
+// This lane's share of super-group g: its U groups' weights summed in
+// increasing id order.  `raw` holds the words when the group is fast.
+template <sv_dtype DT, bool RESID>
+__device__ __forceinline__ float group_lane_sum(const DrawRow& d, int g, int lane, bool fast,
+                                                const GroupRaw<DT, RESID>& raw) {
+    const int e = g * Geom<DT>::kIds + lane * 8;
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < Geom<DT>::kU; ++u) {
+        float zp[8], zq[8], w[8];
+        if (fast) {
+            raw.p[u].unpack(zp);
+            if (RESID) raw.q[u].unpack(zq);
+        } else {
+            load8<DT>(d.prow, d.vocab, e + u * kWave * 8, d.aligned, zp);
+            if (RESID) load8<DT>(d.qrow, d.vocab, e + u * kWave * 8, d.aligned, zq);
+        }
+        weights_from<RESID>(zp, zq, d.c, d.ap, d.isp, d.aq, d.isq, w);
+        acc += sum8(w);
+    }
+    return acc;
+}
+
 // Inverse-CDF draw over one row's weights (RESID: residual of two rows).
-// *mass gets the weight total.  Returns -2 if the total is not positive.
+//  1. Sweep: the row is cut into super-groups of Geom::kIds ids; waves claim
+//     them in turn from an LDS counter (the next one's loads in flight while
+//     the current one is summed) and store each super-group's sum, a fixed
+//     reduction order, in LDS.  No barrier inside the stream.
+//  2. Wave 0 walks the sums in id order (a wave scan), W is their total and
+//     the super-group where the running sum passes v * W is read once more,
+//     Geom::kIdsPerLane consecutive ids per lane, to find the id.
+// If rounding leaves v * W at or above the running total, the last id of
+// positive weight is taken.  Only ids of positive weight are ever drawn.
+// *mass gets W; returns -2 if W is not positive.
 template <sv_dtype DT, bool RESID>
 __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, float ap,
                         float isp, float aq, float isq, float v, DrawSmem& sm, float* mass) {
-    constexpr int U = kDrawUnroll;
+    using G = Geom<DT>;
+    constexpr int kGroupIds = G::kIds;
+    constexpr int kGroupsPerLane = G::kGroupsPerLane;
+    constexpr int kIdsPerLane = G::kIdsPerLane;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
-    const bool aligned = ((reinterpret_cast<uintptr_t>(prow) | reinterpret_cast<uintptr_t>(qrow)) &
-                          15) == 0;
-    const int ntiles = (vocab + kTile - 1) / kTile;
+    DrawRow d;
+    d.prow = prow;
+    d.qrow = qrow;
+    d.vocab = vocab;
+    d.aligned = ((reinterpret_cast<uintptr_t>(prow) | reinterpret_cast<uintptr_t>(qrow)) & 15) == 0;
+    d.c = c;
+    d.ap = ap;
+    d.isp = isp;
+    d.aq = aq;
+    d.isq = isq;
+    const int n_groups = (vocab + kGroupIds - 1) / kGroupIds;
 
-    // sweep: U tiles' loads in flight before any is reduced
-    for (int t0 = 0; t0 < ntiles; t0 += U) {
-        float s[U];
-        if (aligned && (t0 + U) * kTile <= vocab) {
-            Raw8<DT> rp[U], rq[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = (t0 + u) * kTile + tid * 8;
-                rp[u].fetch(prow, e);
-                if (RESID) rq[u].fetch(qrow, e);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float zp[8], zq[8], w[8];
-                rp[u].unpack(zp);
-                if (RESID) rq[u].unpack(zq);
-                weights_from<RESID>(zp, zq, c, ap, isp, aq, isq, w);
-                s[u] = sum8(w);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = (t0 + u) * kTile + tid * 8;
-                float zp[8], zq[8], w[8];
-                load8<DT>(prow, vocab, e, aligned, zp);
-                if (RESID) load8<DT>(qrow, vocab, e, aligned, zq);
-                weights_from<RESID>(zp, zq, c, ap, isp, aq, isq, w);
-                s[u] = sum8(w);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (t0 + u >= ntiles) break;
-            const float ws = wave_sum(s[u]);
-            if (lane == 0) sm.wsum[(t0 + u) * kP2Waves + wave] = ws;
+    // ---- 1. sweep
+    if (tid == 0) sm.next = kP2Waves;
+    __syncthreads();
+    {
+        int g = wave;  // the first claim of each wave is implicit
+        GroupRaw<DT, RESID> cur;
+        bool cur_fast = g < n_groups && group_fast<DT>(d, g);
+        if (cur_fast) group_fetch<DT, RESID>(d, g, lane, cur);
+        while (g < n_groups) {
+            int g2 = 0;
+            if (lane == 0) g2 = atomicAdd(&sm.next, 1);
+            g2 = __builtin_amdgcn_readfirstlane(g2);
+            GroupRaw<DT, RESID> nxt;
+            const bool nxt_fast = g2 < n_groups && group_fast<DT>(d, g2);
+            if (nxt_fast) group_fetch<DT, RESID>(d, g2, lane, nxt);
+            const float gs = wave_sum_dpp(group_lane_sum<DT, RESID>(d, g, lane, cur_fast, cur), lane);
+            if (lane == 0) sm.gsum[g] = gs;
+            g = g2;
+            cur = nxt;
+            cur_fast = nxt_fast;
         }
     }
     __syncthreads();
+
+    // ---- 2. walk and second look (wave 0)
     if (wave == 0) {
-        // tile totals in a fixed order; lane l owns tiles [l*TPL, (l+1)*TPL)
-        float tot[kTilesPerLane];
-        float lane_sum = 0.0f;
+        // lane l owns super-groups [l G, (l + 1) G), G = kGroupsPerLane
+        float lsum = 0.0f;
+        bool lpos = false;
 #pragma unroll
-        for (int i = 0; i < kTilesPerLane; ++i) {
-            const int k = lane * kTilesPerLane + i;
-            float t = 0.0f;
-            if (k < ntiles)
-                for (int w = 0; w < kP2Waves; ++w) t += sm.wsum[k * kP2Waves + w];
-            tot[i] = t;
-            lane_sum += t;
-        }
-        const float incl = wave_incl_scan<float>(lane_sum, lane);
-        float excl = __shfl_up(incl, 1);
-        if (lane == 0) excl = 0.0f;
-        const float W = __shfl(incl, kWave - 1);
-        const float tgt = v * W;
-        // first tile of this lane whose inclusive sum passes tgt, and the sum before it
-        int hit_tile = -1, last_pos_tile = -1;
-        float run = excl, hit_base = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kTilesPerLane; ++i) {
-            const int k = lane * kTilesPerLane + i;
-            const float before = run;
-            run += tot[i];
-            if (k < ntiles && hit_tile < 0 && run > tgt) {
-                hit_tile = k;
-                hit_base = before;
+        for (int i = 0; i < kGroupsPerLane; ++i) {
+            const int g = lane * kGroupsPerLane + i;
+            if (g < n_groups) {
+                lsum += sm.gsum[g];
+                lpos |= sm.gsum[g] > 0.0f;
             }
-            if (k < ntiles && tot[i] > 0.0f) last_pos_tile = k;
         }
-        const uint64_t hits = __ballot(hit_tile >= 0);
-        const uint64_t pos = __ballot(last_pos_tile >= 0);
+        const float incl = wave_incl_sum_dpp(lsum, lane);
+        const float W = lane63(incl);
+        int tok = -2;
+        if (W > 0.0f) {
+            const float tgt = v * W;
+            // the walk, in every lane of wave 0: the first lane holding a
+            // positive super-group whose running sum passes tgt, then its first
+            // positive super-group doing so.  W > 0, so some lane holds a
+            // positive super-group; the walk never leaves the positive ones.
+            const uint64_t pos = __ballot(lpos);
+            const uint64_t past = __ballot(lpos && incl > tgt);
+            bool crossing = past != 0;
+            const int hl = crossing ? __builtin_ctzll(past) : 63 - __builtin_clzll(pos);
+            float run = __shfl(incl - lsum, hl);  // exclusive prefix of lane hl
+            int hit = -1, lastg = -1;
+            float hit_base = 0.0f, last_base = 0.0f;
+            for (int i = 0; i < kGroupsPerLane; ++i) {
+                const int g = hl * kGroupsPerLane + i;
+                if (g >= n_groups) break;
+                const float before = run;
+                run += sm.gsum[g];
+                if (sm.gsum[g] > 0.0f) {
+                    if (crossing && hit < 0 && run > tgt) {
+                        hit = g;
+                        hit_base = before;
+                    }
+                    lastg = g;
+                    last_base = before;
+                }
+            }
+            if (hit < 0) {  // rounding: the last positive id of the lane's last positive group
+                crossing = false;
+                hit = lastg;
+                hit_base = last_base;
+            }
+            // second look: lane l takes ids [g0 + l n, g0 + (l + 1) n), n = kIdsPerLane
+            const int e0 = hit * kGroupIds + lane * kIdsPerLane;
+            float wts[kIdsPerLane];
+            float ls = 0.0f;
+#pragma unroll
+            for (int k8 = 0; k8 < kIdsPerLane / 8; ++k8) {
+                float zp[8], zq[8];
+                const int e = e0 + k8 * 8;
+                if (e < vocab) {
+                    load8<DT>(prow, vocab, e, d.aligned, zp);
+                    if (RESID) load8<DT>(qrow, vocab, e, d.aligned, zq);
+                    weights_from<RESID>(zp, zq, c, ap, isp, aq, isq, wts + k8 * 8);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) wts[k8 * 8 + k] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kIdsPerLane; ++k) ls += wts[k];
+            const float li = wave_incl_sum_dpp(ls, lane);
+            float r2 = hit_base + (li - ls);
+            int cand = 0x7fffffff, lastpos = -1;
+#pragma unroll
+            for (int k = 0; k < kIdsPerLane; ++k) {
+                r2 += wts[k];
+                // Only an id of positive weight can be drawn: the second look and
+                // the sweep round differently, so a lane may start above v * W;
+                // its first positive id is then the crossing.
+                const bool positive = wts[k] > 0.0f;
+                if (crossing && positive && r2 > tgt && cand == 0x7fffffff) cand = e0 + k;
+                if (positive) lastpos = e0 + k;
+            }
+            const uint64_t mc = __ballot(cand != 0x7fffffff);
+            const uint64_t ml = __ballot(lastpos >= 0);
+            if (mc)
+                tok = __builtin_amdgcn_readlane(cand, __builtin_ctzll(mc));
+            else if (ml)
+                tok = __builtin_amdgcn_readlane(lastpos, 63 - __builtin_clzll(ml));
+            else
+                tok = -1;  // unreachable: the group's sum was positive
+        }
         if (lane == 0) {
+            sm.tok = tok;
             sm.total = W;
-            sm.target = tgt;
-            sm.cand = 0x7fffffff;
-            sm.lastpos = -1;
-            sm.tile = -1;
-            sm.base = 0.0f;
-        }
-        if (hits) {
-            if (lane == __builtin_ctzll(hits)) {
-                sm.tile = hit_tile;
-                sm.base = hit_base;
-            }
-        } else if (pos) {
-            // rounding left v * W at or above the total: last id of positive weight
-            if (lane == 63 - __builtin_clzll(pos)) sm.tile = -1 - last_pos_tile;
         }
     }
     __syncthreads();
+    const int tok = sm.tok;
     *mass = sm.total;
-    if (!(sm.total > 0.0f)) {
-        __syncthreads();  // every thread has read sm before a second call rewrites it
-        return -2;
-    }
-    const int tile_code = sm.tile;
-    const bool crossing = tile_code >= 0;
-    const int tile = crossing ? tile_code : -1 - tile_code;
-    const float tgt = sm.target;
-    const int e = tile * kTile + tid * 8;
-    float zp[8], zq[8], w[8];
-    load8<DT>(prow, vocab, e, aligned, zp);
-    if (RESID) load8<DT>(qrow, vocab, e, aligned, zq);
-    weights_from<RESID>(zp, zq, c, ap, isp, aq, isq, w);
-    const float s = sum8(w);
-    // block exclusive scan of the per-thread sums
-    const float incl = wave_incl_scan<float>(s, lane);
-    float excl = __shfl_up(incl, 1);
-    if (lane == 0) excl = 0.0f;
-    if (lane == kWave - 1) sm.wtot[wave] = incl;
-    __syncthreads();
-    float before = sm.base;
-    for (int w2 = 0; w2 < wave; ++w2) before += sm.wtot[w2];
-    float run = before + excl;
-    int cand = 0x7fffffff, lastpos = -1;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        run += w[k];
-        // Only an id of positive weight can be drawn: the scanned prefix and
-        // the per-thread sums round differently, so a thread may start above
-        // v * W; its first positive id is then the crossing.
-        const bool positive = w[k] > 0.0f && e + k < vocab;
-        if (crossing && positive && run > tgt && cand == 0x7fffffff) cand = e + k;
-        if (positive) lastpos = e + k;
-    }
-    cand = wave_min_int(cand);
-    lastpos = wave_max_int(lastpos);
-    if (lane == 0) {
-        atomicMin(&sm.cand, cand);
-        atomicMax(&sm.lastpos, lastpos);
-    }
-    __syncthreads();
-    const int tok = sm.cand != 0x7fffffff ? sm.cand : sm.lastpos;
     __syncthreads();  // sm is reused by a possible second call
     return tok;
 }

@@ -115,6 +115,7 @@ def main():
     row_pos = torch.empty(cap, dtype=torch.int32, device=dev)
     packed = torch.empty(cap, dtype=torch.int32, device=dev)
     ws = torch.zeros(sv.sv_verify_workspace_bytes(n, K), dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(1, sv.sv_budget_workspace_bytes(n, K)), dtype=torch.uint8, device=dev)
     tok_out = torch.empty(n, K + 1, dtype=torch.int32, device=dev)
     acc_out = torch.empty(n, dtype=torch.int32, device=dev)
     p_out = torch.empty(n, K, dtype=torch.float32, device=dev)
@@ -123,7 +124,8 @@ def main():
 
     # set-up pass: the budget's packing decides which target rows the (stand-in)
     # target forward would produce; gather them once into packed buffers
-    sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, kept, budget, survival, err)
+    sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, kept, budget, survival, err,
+                        ws=bws)
     sv.sv_pack_varlen(kept, last_d, toks_d, cu, row_req, row_pos, packed, err)
     torch.cuda.synchronize()
     kept_h = kept.cpu().numpy()
@@ -153,7 +155,7 @@ def main():
         mark(0)
         if kept_in is None:
             sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, kept, budget,
-                                survival, err)
+                                survival, err, ws=bws)
         mark(1)
         if kept_in is None:
             sv.sv_pack_varlen(kept, last_d, toks_d, cu, row_req, row_pos, packed, err)

@@ -63,7 +63,7 @@ typedef enum { SV_STOCHASTIC = 0, SV_GREEDY = 1 } sv_mode;
 
 /* Limits checked on the host. */
 #define SV_MAX_BUDGET_SLOTS 8192   /* n_req and n_req * k_max for sv_budget_select (LDS-resident) */
-#define SV_MAX_DRAFT        64     /* k_max for sv_verify (one wave64 ballot covers a request)   */
+#define SV_MAX_DRAFT        64     /* k_max for sv_verify (one wave64 ballot covers a request) and sv_budget_select */
 #define SV_MAX_VOCAB        1048576
 
 const char* sv_status_str(sv_status s);
@@ -124,11 +124,20 @@ sv_status sv_cost_table_prepare(const float* raw, int32_t raw_len, int32_t granu
  * n_bonus:   bonus tokens (one per sampling request).
  * kept:      [n_req] int32 out.   budget: [1] int32 out (B).
  * survival:  [n_req, k_max] fp32 out, or NULL (0 past draft_len).
- * ws:        sv_budget_workspace_bytes(n_req, k_max) bytes (currently 0).
- * Launch: one workgroup of 1024 threads (LDS-resident sort).
- * Errors: SV_ERR_NULL; SV_ERR_SHAPE if n_req < 0, k_max < 0,
+ * ws:        device scratch of sv_budget_workspace_bytes(n_req, k_max) bytes
+ *            (16 + 8 * n_req * k_max: slot ranks and rank-ordered survivals;
+ *            needs no initialisation, garbage afterwards).  May be NULL when
+ *            that size is 0 (n_req = 0).  Calls that overlap in time must
+ *            not share a workspace.
+ * Launch: two kernels on `stream`.  The first ranks every slot: one
+ * 1024-thread workgroup per 64 slots counts, for each of its slots, the
+ * keys of the whole batch ordered before it (the keys staged in LDS).  The
+ * second, one workgroup of 1024 threads, scans the rank-ordered survivals
+ * and picks B.
+ * Errors: SV_ERR_NULL; SV_ERR_SHAPE if n_req < 0, k_max < 0, k_max > SV_MAX_DRAFT,
  * n_req or n_req * k_max > SV_MAX_BUDGET_SLOTS, or cost_len too short; SV_ERR_VALUE if
- * t_base < 0 or n_bonus < 0.
+ * t_base < 0 or n_bonus < 0; SV_ERR_WORKSPACE if ws is NULL or ws_bytes is
+ * short while the workspace size is nonzero.
  */
 sv_status sv_budget_select(const float* conf, const int32_t* draft_len, int32_t n_req,
                            int32_t k_max, const float* cost, int32_t cost_len, int32_t t_base,

@@ -45,7 +45,13 @@ def test_status_strings():
 def test_workspace_sizes():
     assert sv.sv_verify_workspace_bytes(256, 7) == 256 * 15 * 16
     assert sv.sv_verify_workspace_bytes(-1, 7) == 0
-    assert sv.sv_budget_workspace_bytes(256, 7) == 0
+    # a 16-byte header, then an int32 rank and an fp32 survival per slot
+    assert sv.sv_budget_workspace_bytes(256, 7) == 16 + 1792 * 8
+    assert sv.sv_budget_workspace_bytes(8192, 1) == 16 + 8192 * 8
+    assert sv.sv_budget_workspace_bytes(3, 0) == 16
+    assert sv.sv_budget_workspace_bytes(0, 5) == 0
+    assert sv.sv_budget_workspace_bytes(2048, 5) == 0   # over the slot limit: call is refused
+    assert sv.sv_budget_workspace_bytes(1, 65) == 0     # over the draft limit: call is refused
 
 
 @pytest.mark.parametrize("granule", [1, 2, 16])
@@ -89,12 +95,17 @@ def test_budget_select_host_validation():
     assert budget(k_max=-2) == sv.SV_ERR_SHAPE
     assert budget(n_req=2048, k_max=5, cost_len=20000) == sv.SV_ERR_SHAPE  # > 8192 slots
     assert budget(n_req=8193, k_max=0, cost_len=20000) == sv.SV_ERR_SHAPE  # > 8192 requests
+    assert budget(n_req=1, k_max=65, cost_len=200) == sv.SV_ERR_SHAPE      # > 64 drafts
     assert budget(t_base=-1) == sv.SV_ERR_VALUE
     assert budget(n_bonus=-1) == sv.SV_ERR_VALUE
     assert budget(cost=None) == sv.SV_ERR_NULL
     assert budget(budget=None) == sv.SV_ERR_NULL
     assert budget(conf=None) == sv.SV_ERR_NULL
     assert budget(kept=None) == sv.SV_ERR_NULL
+    need = sv.sv_budget_workspace_bytes(4, 3)
+    assert need > 0
+    assert budget() == sv.SV_ERR_WORKSPACE
+    assert budget(ws=FAKE, ws_bytes=need - 1) == sv.SV_ERR_WORKSPACE
 
 
 def pack(**kw):
