@@ -10,24 +10,6 @@ namespace sv {
 
 constexpr int kWave = 64;
 
-// Per-candidate-row statistics written by verify pass 1 and read by pass 2.
-//   a    : offset in the scaled-logit domain, a = max_x z_x * log2(e) / T
-//          (up to rounding), so that exp2(z * c - a) <= ~1;
-//   s    : sum_x exp2(z_x * c - a); stochastic rows with a fault store -1;
-//   pd   : probability of the position's draft id, exp2(z_d * c - a) / s;
-//   lpd  : (stochastic) log2 of that probability, z_d * c - a - log2(s),
-//          finite even where pd is an fp32 subnormal or zero;
-//   idx  : (greedy) argmax id, -1 for a faulty row.
-struct alignas(16) RowStat {
-    float a;
-    float s;
-    float pd;
-    union {
-        float lpd;
-        int32_t idx;
-    };
-};
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

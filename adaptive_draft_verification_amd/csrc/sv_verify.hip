@@ -128,7 +128,9 @@ __device__ __forceinline__ void merge_as(float& a, float& s, float a2, float s2)
     a = m;
 }
 
-// Exact two-pass row statistics (fallback): offset = max * c, then the sum.
+// Exact two-pass statistics (fallback): offset = max * c, then the sum.  A
+// range holding a NaN or +inf returns S = NaN; one whose logits are all -inf
+// returns (A, S) = (-inf, 0).
 template <sv_dtype DT>
 __device__ void row_stats_exact(const char* row, int vocab, float c, float* red, float* out_a,
                                 float* out_s) {
@@ -136,13 +138,36 @@ __device__ void row_stats_exact(const char* row, int vocab, float c, float* red,
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
     float m = -kInf;
-    for (int e = tid; e < vocab; e += kThreads) m = fmaxf(m, V::load1(row, e));
+    int nan = 0;
+    for (int e = tid; e < vocab; e += kThreads) {
+        const float x = V::load1(row, e);
+        m = fmaxf(m, x);
+        nan |= x != x;
+    }
     m = wave_max(m);
-    if (lane == 0) red[wave] = m;
+    nan = wave_or_int(nan);
+    if (lane == 0) {
+        red[2 * wave] = m;
+        red[2 * wave + 1] = nan ? 1.0f : 0.0f;
+    }
     __syncthreads();
     float mx = red[0];
-    for (int w = 1; w < kThreads / kWave; ++w) mx = fmaxf(mx, red[w]);
+    bool any_nan = red[1] != 0.0f;
+    for (int w = 1; w < kThreads / kWave; ++w) {
+        mx = fmaxf(mx, red[2 * w]);
+        any_nan |= red[2 * w + 1] != 0.0f;
+    }
     __syncthreads();
+    if (any_nan || mx == kInf) {  // block-uniform
+        *out_a = 0.0f;
+        *out_s = __builtin_nanf("");
+        return;
+    }
+    if (mx == -kInf) {
+        *out_a = -kInf;
+        *out_s = 0.0f;
+        return;
+    }
     const float a = mx * c;
     float s = 0.0f;
     for (int e = tid; e < vocab; e += kThreads) s += fast_exp2(fmaf(V::load1(row, e), c, -a));
@@ -332,6 +357,38 @@ __device__ void row_argmax(const char* row, int vocab, float* redf, int* redi, f
     *out_nan = nan_i != 0;
 }
 
+// Per-part statistics written by verify pass 1 and merged by pass 2.  A row
+// is cut into row_parts(vocab) contiguous parts of part_len ids (a multiple
+// of 8, so every part starts 16-byte aligned), one workgroup each.
+//   a   : stochastic: offset, max_x z_x * log2(e)/T over the part (up to
+//         rounding), -inf for a part without a finite logit; greedy: the
+//         part's max logit;
+//   s   : stochastic: sum_x exp2(z_x * log2(e)/T - a) over the part; 0 for a
+//         part without a finite logit; -1 if the part holds a NaN or +inf;
+//   zd  : stochastic: the logit of the position's draft id when it lies in
+//         this part;
+//   idx : greedy: the lowest id reaching the part's max (INT_MAX if every
+//         logit is -inf), -1 if the part holds a NaN.
+struct alignas(16) PartStat {
+    float a;
+    float s;
+    float zd;
+    int32_t idx;
+};
+constexpr int kMaxParts = 8;
+#ifndef SV_PART_IDS
+#define SV_PART_IDS 65536
+#endif
+constexpr int kPartIds = SV_PART_IDS;  // parts of about this many ids
+
+__device__ __forceinline__ int row_parts(int vocab) {
+    const int h = (vocab + kPartIds - 1) / kPartIds;
+    return h < 1 ? 1 : (h > kMaxParts ? kMaxParts : h);
+}
+__device__ __forceinline__ int part_len(int vocab, int parts) {
+    return ((vocab + parts - 1) / parts + 7) & ~7;
+}
+
 struct Args {
     const char* target;
     int64_t target_ld_bytes;
@@ -345,7 +402,7 @@ struct Args {
     float c;  // log2(e) / T
     uint64_t seed;
     uint64_t step;
-    RowStat* stats;  // [n, 2*k_max + 1]
+    PartStat* stats;  // [n, 2*k_max + 1, kMaxParts]
     int32_t* out_tokens;
     int32_t* out_accepted;
     float* out_p;
@@ -662,8 +719,81 @@ __device__ void emit_fault(const Args& a, int r, int bits) {
     }
 }
 
+// Statistics of one row, merged from its parts.
+struct RowMerged {
+    float A, S;      // stochastic: offset and sum over the row
+    float pd, lpd;   // stochastic: p(d) and log2 p(d) of the position's draft id
+    float mx;        // greedy: the row's max logit
+    int idx;         // greedy: lowest id reaching it
+    bool fault;      // NaN or +inf somewhere, or no finite mass
+};
+
+// Merge the parts of one row in part order (deterministic).  d: the draft id
+// whose probability is wanted, or -1.
+template <bool GREEDY>
+__device__ RowMerged merge_parts(const PartStat* ps, int parts, int plen, int d, float c) {
+    PartStat p[kMaxParts];
+#pragma unroll
+    for (int h = 0; h < kMaxParts; ++h)
+        if (h < parts) p[h] = ps[h];
+    RowMerged m;
+    m.A = -kInf;
+    m.S = 0.0f;
+    m.pd = -1.0f;
+    m.lpd = -kInf;
+    m.mx = -kInf;
+    m.idx = 0x7fffffff;
+    m.fault = false;
+    if (GREEDY) {
+#pragma unroll
+        for (int h = 0; h < kMaxParts; ++h) {
+            if (h >= parts) break;
+            if (p[h].idx < 0) m.fault = true;                   // a NaN in the part
+            if (p[h].a > m.mx) {                                 // first part wins ties
+                m.mx = p[h].a;
+                m.idx = p[h].idx;
+            }
+        }
+        if (m.mx == kInf || m.mx == -kInf) m.fault = true;
+        return m;
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxParts; ++h) {
+        if (h >= parts) break;
+        if (!(p[h].s >= 0.0f)) {
+            m.fault = true;  // NaN or +inf in the part
+        } else if (p[h].s > 0.0f) {
+            if (m.S == 0.0f) {
+                m.A = p[h].a;
+                m.S = p[h].s;
+            } else {
+                merge_as(m.A, m.S, p[h].a, p[h].s);
+            }
+        }
+    }
+    if (!(m.S > 0.0f) || !is_finite_bits(m.S) || !is_finite_bits(m.A)) m.fault = true;
+    if (d >= 0 && !m.fault) {
+        // part d / plen holds d's logit; its scaled log-probability is finite
+        // even where p(d) is an fp32 subnormal or zero
+        const int hd = d / plen;
+        float zd = 0.0f;
+#pragma unroll
+        for (int h = 0; h < kMaxParts; ++h)
+            if (h == hd) zd = p[h].zd;
+        const float y = fmaf(zd, c, -m.A);
+        m.pd = exp2f(y) / m.S;
+        m.lpd = y - log2f(m.S);
+    }
+    return m;
+}
+
 struct FinishSmem {
     DrawSmem draw;
+    float ta[kWave], ts[kWave], qa[kWave], qs[kWave];  // merged rows of position j
+    float tpd[kWave], qpd[kWave];                      // p(d_j), q(d_j)
+    int gidx[kWave];                                   // greedy: argmax of target row j
+    float ba, bs;                                      // bonus row b (stochastic)
+    int bidx;                                          // bonus row b (greedy)
     int L, b, lo, fault;
 };
 
@@ -671,8 +801,11 @@ template <sv_dtype DT, bool GREEDY>
 __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
     const int tid = threadIdx.x;
     const int k_max = a.k_max;
-    const RowStat* st = a.stats + (int64_t)r * (2 * k_max + 1);
+    const int parts = row_parts(a.vocab), plen = part_len(a.vocab, parts);
+    const PartStat* st = a.stats + (int64_t)r * (2 * k_max + 1) * kMaxParts;
     if (tid < kWave) {
+        // lane j: position j (target row j and draft row j); lane 0 also
+        // merges the bonus row b
         const int lane = tid;
         const int lo = a.cu_rows[r], hi = a.cu_rows[r + 1];
         const int b = hi - lo - 1;
@@ -684,23 +817,40 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
             const int j = lane;
             if (j < b) {
                 const int d = a.draft_tokens[(int64_t)r * k_max + j];
-                if (d < 0 || d >= a.vocab) fault |= SV_DEV_BAD_TOKEN;
-                const RowStat ts = st[j];
+                const bool d_ok = d >= 0 && d < a.vocab;
+                if (!d_ok) fault |= SV_DEV_BAD_TOKEN;
+                const RowMerged t = merge_parts<GREEDY>(st + (int64_t)j * kMaxParts, parts,
+                                                        plen, d_ok ? d : -1, a.c);
+                if (t.fault) fault |= SV_DEV_NONFINITE;
                 if (GREEDY) {
-                    if (ts.idx < 0) fault |= SV_DEV_NONFINITE;
-                    acc = ts.idx == d;
+                    acc = t.idx == d;
+                    sm.gidx[j] = t.idx;
                 } else {
-                    const RowStat ds = st[k_max + 1 + j];
-                    if (!(ts.s > 0.0f) || !(ds.s > 0.0f)) fault |= SV_DEV_NONFINITE;
+                    const RowMerged q = merge_parts<false>(
+                        st + (int64_t)(k_max + 1 + j) * kMaxParts, parts, plen, d_ok ? d : -1,
+                        a.c);
+                    if (q.fault) fault |= SV_DEV_NONFINITE;
                     float u, v;
                     draw_uniforms(a.seed, a.step, (uint32_t)r, (uint32_t)j, &u, &v);
                     // u < min(1, p/q), the ratio taken from log2 p - log2 q so that
                     // probabilities below fp32's normal range do not decide it
-                    acc = u < exp2f(ts.lpd - ds.lpd);
+                    acc = u < exp2f(t.lpd - q.lpd);
+                    sm.ta[j] = t.A;
+                    sm.ts[j] = t.S;
+                    sm.qa[j] = q.A;
+                    sm.qs[j] = q.S;
+                    sm.tpd[j] = t.pd;
+                    sm.qpd[j] = q.pd;
                 }
             }
-            if (lane == 0 && (GREEDY ? st[b].idx < 0 : !(st[b].s > 0.0f)))
-                fault |= SV_DEV_NONFINITE;
+            if (lane == 0) {
+                const RowMerged t = merge_parts<GREEDY>(st + (int64_t)b * kMaxParts, parts,
+                                                        plen, -1, a.c);
+                if (t.fault) fault |= SV_DEV_NONFINITE;
+                sm.ba = t.A;
+                sm.bs = t.S;
+                sm.bidx = t.idx;
+            }
         }
         fault = wave_or_int(fault);
         const uint64_t rej = __ballot(!acc);
@@ -720,25 +870,24 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
     int token;
     float mass = -1.0f;
     if (GREEDY) {
-        token = st[L].idx;
+        token = L < b ? sm.gidx[L] : sm.bidx;
     } else {
         float u, v;
         draw_uniforms(a.seed, a.step, (uint32_t)r, (uint32_t)L, &u, &v);
-        const RowStat tp = st[L];
         const char* prow = a.target + ((int64_t)lo + L) * a.target_ld_bytes;
         if (L < b) {
-            const RowStat tq = st[k_max + 1 + L];
+            const float tA = sm.ta[L], tS = sm.ts[L];
             const char* qrow = a.draft + ((int64_t)r * k_max + L) * a.draft_ld_bytes;
-            token = draw_row<DT, true>(prow, qrow, a.vocab, a.c, tp.a, 1.0f / tp.s, tq.a,
-                                       1.0f / tq.s, v, sm.draw, &mass);
+            token = draw_row<DT, true>(prow, qrow, a.vocab, a.c, tA, 1.0f / tS, sm.qa[L],
+                                       1.0f / sm.qs[L], v, sm.draw, &mass);
             if (token == -2) {  // zero residual mass: draw from p instead
                 float unused;
-                token = draw_row<DT, false>(prow, prow, a.vocab, a.c, tp.a, 1.0f, 0.0f, 1.0f, v,
+                token = draw_row<DT, false>(prow, prow, a.vocab, a.c, tA, 1.0f, 0.0f, 1.0f, v,
                                             sm.draw, &unused);
             }
         } else {
             float unused;
-            token = draw_row<DT, false>(prow, prow, a.vocab, a.c, tp.a, 1.0f, 0.0f, 1.0f, v,
+            token = draw_row<DT, false>(prow, prow, a.vocab, a.c, sm.ba, 1.0f, 0.0f, 1.0f, v,
                                         sm.draw, &unused);
         }
     }
@@ -756,8 +905,8 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
     for (int j = tid; j < k_max; j += blockDim.x) {
         float p = -1.0f, q = -1.0f;
         if (!GREEDY && j < b) {
-            p = st[j].pd;
-            q = st[k_max + 1 + j].pd;
+            p = sm.tpd[j];
+            q = sm.qpd[j];
         }
         if (a.out_p) a.out_p[(int64_t)r * k_max + j] = p;
         if (a.out_q) a.out_q[(int64_t)r * k_max + j] = q;
@@ -771,12 +920,26 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
 // ------------------------------------------------------------------ kernels
 
 // Pass-1 workgroup g -> (request, slot).  Groups of n workgroups run the same
-// row kind for every request: target row K first, then for j = K-1 .. 0 draft
-// row j and target row j.  Slots: target j = j, draft j = k_max + 1 + j.
+// row kind for every request.  Slots: target j = j, draft j = k_max + 1 + j.
+#ifndef SV_PASS1_ASCENDING
+#define SV_PASS1_ASCENDING 1
+#endif
 __device__ __forceinline__ void pass1_slot(int g, int n_req, int k_max, bool greedy, int* r,
                                            int* slot) {
     const int grp = g / n_req;
     *r = g - grp * n_req;
+#if SV_PASS1_ASCENDING
+    // position 0 first: every request verifies its low positions, so the
+    // workgroups that find no row (positions past a request's budget) come
+    // last, where they overlap the tail instead of delaying the stream
+    if (greedy) {
+        *slot = grp;
+        return;
+    }
+    const int j = grp >> 1;
+    *slot = (grp & 1) == 0 ? j : k_max + 1 + j;
+#else
+    // target K first, then for j = K-1 .. 0 draft row j and target row j
     if (greedy) {
         *slot = k_max - grp;
         return;
@@ -787,14 +950,16 @@ __device__ __forceinline__ void pass1_slot(int g, int n_req, int k_max, bool gre
     }
     const int j = k_max - 1 - (grp - 1) / 2;
     *slot = ((grp - 1) & 1) == 0 ? k_max + 1 + j : j;
+#endif
 }
 
 template <sv_dtype DT, bool GREEDY>
-__global__ __launch_bounds__(kThreads) void rowstats_kernel(Args a, int n_req) {
+__global__ __launch_bounds__(kThreads) void rowstats_kernel(Args a, int n_req, int parts) {
     __shared__ float redf[2 * (kThreads / kWave)];
     __shared__ int redi[2 * (kThreads / kWave)];
+    const int h = blockIdx.x % parts;
     int r, slot;
-    pass1_slot(blockIdx.x, n_req, a.k_max, GREEDY, &r, &slot);
+    pass1_slot(blockIdx.x / parts, n_req, a.k_max, GREEDY, &r, &slot);
     const int lo = a.cu_rows[r], hi = a.cu_rows[r + 1];
     const int b = hi - lo - 1;
     if (lo < 0 || b < 0 || b > a.k_max || (int64_t)hi > a.target_rows) return;
@@ -803,36 +968,39 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(Args a, int n_req) {
     if (is_draft ? (j >= b) : (j > b)) return;
     const char* row = is_draft ? a.draft + ((int64_t)r * a.k_max + j) * a.draft_ld_bytes
                                : a.target + ((int64_t)lo + j) * a.target_ld_bytes;
-    RowStat* out = a.stats + (int64_t)r * (2 * a.k_max + 1) + slot;
+    // this workgroup's part of the row: ids [p0, p1)
+    const int plen = part_len(a.vocab, parts);
+    const int p0 = min(a.vocab, h * plen), p1 = min(a.vocab, p0 + plen);
+    const char* prow = row + (int64_t)p0 * Vec<DT>::kBytes;
+    PartStat* out = a.stats + ((int64_t)r * (2 * a.k_max + 1) + slot) * kMaxParts + h;
     if (GREEDY) {
         float mx;
         int idx;
         bool nan;
-        row_argmax<DT>(row, a.vocab, redf, redi, &mx, &idx, &nan);
+        row_argmax<DT>(prow, p1 - p0, redf, redi, &mx, &idx, &nan);
         if (threadIdx.x == 0) {
-            const bool fault = nan || mx == kInf || mx == -kInf;
-            RowStat st{};
+            PartStat st{};
             st.a = mx;
-            st.idx = fault ? -1 : idx;
+            st.idx = nan ? -1 : (idx == 0x7fffffff ? idx : p0 + idx);
             *out = st;
         }
         return;
     }
     // the draft id's logit is fetched up front so its latency hides under the stream
     const int d = j < b ? a.draft_tokens[(int64_t)r * a.k_max + j] : -1;
-    const bool want_pd = d >= 0 && d < a.vocab;
+    const bool want_zd = d >= p0 && d < p1;
     float zd = 0.0f;
-    if (threadIdx.x == 0 && want_pd) zd = Vec<DT>::load1(row, d);
+    if (threadIdx.x == 0 && want_zd) zd = Vec<DT>::load1(row, d);
     float A, S;
-    row_stats_stochastic<DT>(row, a.vocab, a.c, redf, &A, &S);
+    row_stats_stochastic<DT>(prow, p1 - p0, a.c, redf, &A, &S);
     if (threadIdx.x == 0) {
-        const bool fault = !(S > 0.0f) || !is_finite_bits(S) || !is_finite_bits(A);
-        const float y = fmaf(zd, a.c, -A);
-        RowStat st;
-        st.a = A;
+        // S is NaN or +inf for a faulty part, 0 (A = -inf) for one without mass
+        const bool fault = !(S >= 0.0f) || !is_finite_bits(S) || (S > 0.0f && !is_finite_bits(A));
+        PartStat st;
+        st.a = fault ? 0.0f : A;
         st.s = fault ? -1.0f : S;
-        st.pd = want_pd ? exp2f(y) / S : -1.0f;
-        st.lpd = want_pd ? y - log2f(S) : -kInf;
+        st.zd = zd;
+        st.idx = 0;
         *out = st;
     }
 }
@@ -843,18 +1011,25 @@ __global__ __launch_bounds__(GREEDY ? kWave : kP2Threads) void decide_kernel(Arg
     finish_request<DT, GREEDY>(a, blockIdx.x, fin);
 }
 
+int host_row_parts(int vocab) {
+    const int h = (vocab + kPartIds - 1) / kPartIds;
+    return h < 1 ? 1 : (h > kMaxParts ? kMaxParts : h);
+}
+
 template <sv_dtype DT, bool GREEDY>
 hipError_t launch_typed(const VerifyArgs& v, hipStream_t stream) {
     const int esize = Vec<DT>::kBytes;
     Args a{static_cast<const char*>(v.target), v.target_ld * esize, v.target_rows,
            static_cast<const char*>(v.draft), v.draft_ld * esize, v.vocab, v.draft_tokens,
            v.cu_rows, v.k_max, kLog2e / v.temperature, v.seed, v.step,
-           static_cast<RowStat*>(v.ws), v.out_tokens, v.out_accepted, v.out_p_draft,
+           static_cast<PartStat*>(v.ws), v.out_tokens, v.out_accepted, v.out_p_draft,
            v.out_q_draft, v.out_residual_mass, v.dev_error};
     const int slots = GREEDY ? v.k_max + 1 : 2 * v.k_max + 1;
     if (v.stages & 1) {
-        hipLaunchKernelGGL((rowstats_kernel<DT, GREEDY>), dim3((unsigned)(v.n_req * slots)),
-                           dim3(kThreads), 0, stream, a, v.n_req);
+        const int parts = host_row_parts(v.vocab);
+        hipLaunchKernelGGL((rowstats_kernel<DT, GREEDY>),
+                           dim3((unsigned)(v.n_req * slots * parts)), dim3(kThreads), 0, stream, a,
+                           v.n_req, parts);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -878,7 +1053,7 @@ __global__ void philox_uniforms_kernel(uint64_t seed, uint64_t step, int n_req, 
 }  // namespace
 
 size_t verify_workspace_bytes(int n_req, int k_max) {
-    return (size_t)n_req * (size_t)(2 * k_max + 1) * sizeof(RowStat);
+    return (size_t)n_req * (size_t)(2 * k_max + 1) * kMaxParts * sizeof(PartStat);
 }
 
 hipError_t launch_verify(const VerifyArgs& v, hipStream_t stream) {

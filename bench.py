@@ -2,24 +2,27 @@
 
 A step is one pass of the whole path on one batch: adaptive budget selection
 (sv_budget_select), varlen packing (sv_pack_varlen) and full-vocabulary
-verification (sv_verify: row statistics, then each request's decisions and
-draw by the last of its workgroups), each stage reading the previous stage's
-device output.  The default workload
-is 256 requests with 7 drafts each over a 129280-token vocabulary, bf16
-logits, confidences X^j with X ~ Beta(8, 2), and a cost table padded to
-multiples of 16 tokens (workloads.make("b256_v129280")); the budget decides
-how many rows each request verifies.
+verification (sv_verify: row statistics, then one workgroup per request that
+decides and draws), each stage reading the previous stage's device output.
+The default workload is 256 requests with 7 drafts each over a 129280-token
+vocabulary, bf16 logits, confidences X^j with X ~ Beta(8, 2), and a cost
+table padded to multiples of 16 tokens (workloads.make("b256_v129280")); the
+budget decides how many rows each request verifies.
 
 Inputs are generated once on the host and copied to HBM before timing; two
 replicas of the logit buffers alternate between steps so that reads come from
-HBM rather than the 256 MB Infinity Cache.  HIP events on the launch stream
-time every stage; `value` is target rows verified per second of whole-step
-time, and the roofline is pass 1's algorithmic bytes (every kept row once)
-over its event time; pass 2's bytes (the rows each draw reads again) are
-reported beside it.  A second
-leg verifies every draft (full K: 2048 target + 1792 draft rows) for the
-bandwidth figure at the largest size.  The CPU oracle runs one
-step of the same workload on the host for the cpu_baseline figure.
+HBM rather than the 256 MB Infinity Cache.  The headline times K steps
+launched back to back (--graph replays them from HIP graphs instead, one per
+replica and Philox step, in turn); `value` is target rows verified per second
+of that wall time.  A separate loop with HIP events on the launch stream times
+every stage; the roofline is pass 1's algorithmic bytes (every kept row once)
+over its mean launch time (K launches back to back between two events), with
+the HBM bytes the byte counters measured for it
+(profiles/, while the kernel's sources are unchanged); pass 2's bytes (the
+rows each draw reads again) are reported beside it.  A second leg verifies
+every draft (full K: 2048 target + 1792 draft rows) for the bandwidth figure
+at the largest size.  The CPU oracle runs whole steps of the same workload on
+the host for the cpu_baseline figure.
 
 Prints one JSON line.
 """
@@ -53,7 +56,58 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="lower bound on the oracle's timed host work")
+    ap.add_argument("--graph", dest="graph", action="store_true", default=False,
+                    help="time steps replayed from HIP graphs (slower than eager launches "
+                         "on ROCm 7.2: ~130 vs ~122 us per step)")
+    ap.add_argument("--eager", dest="graph", action="store_false",
+                    help="time eagerly launched steps (default)")
+    ap.add_argument("--graphs", type=int, default=4,
+                    help="graphs captured (one per replica and Philox step), replayed in turn")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only copy a device buffer of this many MiB three times and exit: "
+                         "a plain copy of known size, to scale HBM byte counters by")
     return ap.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "verify_pass1_b256_v129280_hbm_bytes.md")
+
+
+def measured_traffic(workload, mode):
+    """Pass-1 HBM bytes per launch from the committed rocprofv3 byte-counter
+    summary, or None unless it covers this workload and mode and the kernel's
+    sources still hash as they did when the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    wl = re.search(r"^workload: (\S+) (\S+)$", text, re.M)
+    tb = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    hs = re.search(r"^sources_sha256: ([0-9a-f]{64})$", text, re.M)
+    srcs = re.search(r"^sources: (.+)$", text, re.M)
+    if not (wl and tb and hs and srcs) or wl.groups() != (workload, mode):
+        return None
+    h = hashlib.sha256()
+    for f in srcs.group(1).split():
+        try:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        except OSError:
+            return None
+    return int(tb.group(1)) if h.hexdigest() == hs.group(1) else None
+
+
+def copy_calibration(mib):
+    """Three device-to-device copies of `mib` MiB (read mib, write mib each)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
 def main():
@@ -63,6 +117,10 @@ def main():
               f"(asked for --gpus {args.gpus}); the verify step shards by request with no "
               f"exchange, see the design notes.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+        return
 
     import torch
 
@@ -192,16 +250,74 @@ def main():
             raise RuntimeError(f"device error bits {int(err.item())} during the benchmark")
         return wall_, ms
 
+    def timed_plain(iters, fn):
+        """Wall time of `iters` steps with nothing else on the stream."""
+        torch.cuda.synchronize()
+        t0_ = time.perf_counter()
+        for i in range(iters):
+            fn(i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0_
+
+    # the headline: K steps back to back, launched eagerly or replayed from HIP
+    # graphs (one per replica and Philox step, cycled)
+    graphs = []
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(2):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(args.graphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_step(i):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(i)
+
     for i in range(args.warmup):
+        run_step(i)
+    wall = timed_plain(args.steps, run_step)
+    wall_eager = timed_plain(args.steps, step) if graphs else wall
+    # per-stage times in a separate loop (events between stages cost time)
+    for i in range(2):
         step(i)
-    wall, stage_ms = timed(args.steps)
+    _, stage_ms = timed(args.steps)
     p2_rows = pass2_rows(range(args.steps), kept_h)
+
+    def pass1_launch_ms(iters, reps=None, cu_rows=None):
+        """Mean duration of the roofline kernel: `iters` pass-1 launches back to
+        back (replicas alternating) between two events on the launch stream."""
+        reps = reps or replicas
+        cu_i = cu if cu_rows is None else cu_rows
+        for i in range(2):
+            tp_, dr_ = reps[i % len(reps)]
+            sv.sv_verify_stages(tp_, dr_, toks_d, cu_i, mode, w.tau, w.seed, i, tok_out,
+                                acc_out, ws, 1, p_out, q_out, res_out, err, vocab=V)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(iters):
+            tp_, dr_ = reps[i % len(reps)]
+            sv.sv_verify_stages(tp_, dr_, toks_d, cu_i, mode, w.tau, w.seed, i, tok_out,
+                                acc_out, ws, 1, p_out, q_out, res_out, err, vocab=V)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
 
     ms_per_step = wall * 1e3 / args.steps
     pass1_ms, pass2_ms = float(np.mean(stage_ms[:, 2])), float(np.mean(stage_ms[:, 3]))
+    roof_ms = pass1_launch_ms(args.steps)
     pass1_bytes = (rows_t + (rows_d if mode == sv.SV_STOCHASTIC else 0)) * V * esize
     pass2_bytes = float(np.mean(p2_rows)) * V * esize
-    achieved = pass1_bytes / (pass1_ms * 1e-3) / 1e9
+    achieved = pass1_bytes / (roof_ms * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- full K leg
     full = None
@@ -255,6 +371,7 @@ def main():
                          f"verify of {rows_t} target rows each, Philox step varied) with numpy "
                          f"fp64 on one host thread, {t_cpu:.1f} s"}
 
+    traffic = measured_traffic(args.workload, args.mode)
     out = {
         "metric": METRIC,
         "value": round(rows_t / (ms_per_step * 1e-3), 1),
@@ -276,14 +393,17 @@ def main():
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "rowstats_kernel (verify pass 1)",
-                     "bytes_per_launch": int(pass1_bytes)},
+                     "traffic": traffic, "kernel": "rowstats_kernel (verify pass 1)",
+                     "bytes_per_launch": int(pass1_bytes),
+                     "launch_us": round(roof_ms * 1e3, 2)},
         "budget_select_us": round(float(np.mean(stage_ms[:, 0])) * 1e3, 2),
         "pack_us": round(float(np.mean(stage_ms[:, 1])) * 1e3, 2),
         "verify_pass1_us": round(pass1_ms * 1e3, 2),
         "verify_pass2_us": round(pass2_ms * 1e3, 2),
         "verify_pass2_bytes": int(pass2_bytes),
         "gpu_step_us": round(float(np.mean(stage_ms.sum(axis=1))) * 1e3, 2),
+        "launch": "hip-graph replay" if graphs else "eager",
+        "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 4),
         "step_hbm_gbps": round((pass1_bytes + pass2_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
         "full_k": full,
         "cpu_baseline": cpu,

@@ -19,6 +19,7 @@ sv = pytest.importorskip("adaptive_draft_verification_amd",
                          reason="libspecverify.so not built (python adaptive_draft_verification_amd/build.py)")
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+WS43 = sv.sv_verify_workspace_bytes(4, 3)  # the verify calls below: 4 requests, k_max 3
 
 
 def declared_functions():
@@ -43,7 +44,7 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    assert sv.sv_verify_workspace_bytes(256, 7) == 256 * 15 * 16
+    assert sv.sv_verify_workspace_bytes(256, 7) == 256 * 15 * 8 * 16  # 8 parts per row, 16 B each
     assert sv.sv_verify_workspace_bytes(-1, 7) == 0
     # a 16-byte header, then an int32 rank and an fp32 survival per slot
     assert sv.sv_budget_workspace_bytes(256, 7) == 16 + 1792 * 8
@@ -128,7 +129,7 @@ def verify(**kw):
                 dtype=sv.SV_F32, vocab=32, draft_tokens=FAKE, cu_rows=FAKE, n_req=4, k_max=3,
                 mode=sv.SV_STOCHASTIC, temperature=1.0, seed=0, step=0, out_tokens=FAKE,
                 out_accepted=FAKE, out_p=None, out_q=None, out_resid=None, dev_error=None,
-                ws=FAKE, ws_bytes=4 * 7 * 16, stream=None)
+                ws=FAKE, ws_bytes=WS43, stream=None)
     args.update(kw)
     return sv._lib.sv_verify(*args.values())
 
@@ -148,7 +149,7 @@ def test_verify_host_validation():
     assert verify(temperature=float("nan")) == sv.SV_ERR_VALUE
     assert verify(temperature=float("inf")) == sv.SV_ERR_VALUE
     assert verify(temperature=1e-39) == sv.SV_ERR_VALUE
-    assert verify(ws_bytes=4 * 7 * 16 - 1) == sv.SV_ERR_WORKSPACE
+    assert verify(ws_bytes=WS43 - 1) == sv.SV_ERR_WORKSPACE
     assert verify(ws=None) == sv.SV_ERR_WORKSPACE
     for key in ("target", "cu_rows", "out_tokens", "out_accepted", "draft_tokens", "draft"):
         assert verify(**{key: None}) == sv.SV_ERR_NULL, key
@@ -165,7 +166,7 @@ def test_verify_stages_validation():
                 dtype=sv.SV_F32, vocab=32, draft_tokens=FAKE, cu_rows=FAKE, n_req=4, k_max=3,
                 mode=sv.SV_STOCHASTIC, temperature=1.0, seed=0, step=0, out_tokens=FAKE,
                 out_accepted=FAKE, out_p=None, out_q=None, out_resid=None, dev_error=None,
-                ws=FAKE, ws_bytes=4 * 7 * 16)
+                ws=FAKE, ws_bytes=WS43)
     for bad in (0, 4, -1):
         assert sv._lib.sv_verify_stages(*base.values(), bad, None) == sv.SV_ERR_VALUE
     base["ws"] = None

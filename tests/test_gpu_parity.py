@@ -333,3 +333,63 @@ def test_end_to_end_path_on_device():
     g = {k: t.cpu().numpy() for k, t in v.items()}
     compare_verify(g, target, draft, toks, o_p["cu_rows"], w.k_max, w.vocab, "stochastic", w.tau,
                    w.seed, w.step)
+
+
+def test_graph_replay_matches_eager():
+    """The whole step captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager result bit for bit."""
+    import adaptive_draft_verification_amd as sv
+    w = workloads.make("b16_v32000")
+    cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+    o_b = oracle.budget_select(w.conf, w.draft_len, w.k_max, cost, w.t_base, w.n_bonus)
+    toks = w.draft_tokens("stochastic")
+    o_p = oracle.pack_varlen(o_b["kept"], w.last_token, toks, w.k_max)
+    target = workloads.assemble_target(w, o_p["cu_rows"], o_b["kept"])
+    draft = workloads.assemble_draft(w, o_b["kept"])
+    dt = logits_dtype(w)
+    n, k = w.n, w.k_max
+    dev = torch.device("cuda")
+    conf_d, dl_d, cost_d = to_dev(w.conf), to_dev(w.draft_len), to_dev(cost)
+    last_d, toks_d = to_dev(w.last_token), to_dev(toks)
+    tgt_d, drf_d = to_dev(target, dt), to_dev(draft, dt)
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(kept=torch.empty(n, **i32), budget=torch.empty(1, **i32),
+               cu=torch.empty(n + 1, **i32), row_req=torch.empty(n * (k + 1), **i32),
+               row_pos=torch.empty(n * (k + 1), **i32), packed=torch.empty(n * (k + 1), **i32),
+               tokens=torch.empty(n, k + 1, **i32), accepted=torch.empty(n, **i32),
+               err=torch.zeros(1, **i32))
+    bws = torch.empty(max(1, sv.sv_budget_workspace_bytes(n, k)), dtype=torch.uint8, device=dev)
+    vws = torch.zeros(sv.sv_verify_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+
+    def step(s):
+        sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, out["kept"],
+                            out["budget"], None, out["err"], ws=bws)
+        sv.sv_pack_varlen(out["kept"], last_d, toks_d, out["cu"], out["row_req"],
+                          out["row_pos"], out["packed"], out["err"])
+        sv.sv_verify(tgt_d, drf_d, toks_d, out["cu"], sv.SV_STOCHASTIC, w.tau, w.seed, s,
+                     out["tokens"], out["accepted"], vws, dev_error=out["err"], vocab=w.vocab)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {key: t.cpu().numpy().copy() for key, t in out.items()}
+
+    step(5)
+    want = snapshot()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(5)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(5)
+    for rep in range(4):
+        step(6 + rep)  # eager work that changes every output in between
+        other = snapshot()
+        g.replay()
+        got = snapshot()
+        for key in want:
+            np.testing.assert_array_equal(got[key], want[key], err_msg=f"replay {rep}: {key}")
+        assert not np.array_equal(other["tokens"], want["tokens"])
+    assert int(want["err"][0]) == 0
