@@ -270,17 +270,26 @@ def pack_varlen(kept, last_token, draft_tokens, stream=None):
 
 
 def verify(target, draft, draft_tokens, cu_rows, mode, temperature=1.0, seed=0, step=0,
-           vocab=None, stream=None):
+           vocab=None, stream=None, stages=None, ws=None):
+    """Allocating wrapper: sv_verify (one launch), or sv_verify_stages(stages) (the
+    two-launch path) when `stages` is given.  ws: a zero-filled workspace to reuse."""
     dev = target.device
     n, k_max = draft_tokens.shape
-    ws = torch.zeros(max(1, sv_verify_workspace_bytes(n, k_max)), dtype=torch.uint8, device=dev)
+    if ws is None:
+        ws = torch.zeros(max(1, sv_verify_workspace_bytes(n, k_max)), dtype=torch.uint8,
+                         device=dev)
     out = dict(tokens=torch.empty(n, k_max + 1, dtype=torch.int32, device=dev),
                accepted=torch.empty(n, dtype=torch.int32, device=dev),
                p_draft=torch.empty(n, k_max, dtype=torch.float32, device=dev),
                q_draft=torch.empty(n, k_max, dtype=torch.float32, device=dev),
                residual_mass=torch.empty(n, dtype=torch.float32, device=dev),
                dev_error=torch.zeros(1, dtype=torch.int32, device=dev))
-    sv_verify(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
-              out["tokens"], out["accepted"], ws, out["p_draft"], out["q_draft"],
-              out["residual_mass"], out["dev_error"], vocab, stream)
+    if stages is None:
+        sv_verify(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
+                  out["tokens"], out["accepted"], ws, out["p_draft"], out["q_draft"],
+                  out["residual_mass"], out["dev_error"], vocab, stream)
+    else:
+        sv_verify_stages(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
+                         out["tokens"], out["accepted"], ws, stages, out["p_draft"],
+                         out["q_draft"], out["residual_mass"], out["dev_error"], vocab, stream)
     return out

@@ -393,3 +393,24 @@ def test_graph_replay_matches_eager():
             np.testing.assert_array_equal(got[key], want[key], err_msg=f"replay {rep}: {key}")
         assert not np.array_equal(other["tokens"], want["tokens"])
     assert int(want["err"][0]) == 0
+
+
+def test_verify_reuses_an_uncleared_workspace():
+    """Calls on one workspace that is never cleared (filled with garbage first):
+    each equals a call on a fresh workspace."""
+    import adaptive_draft_verification_amd as sv
+    rng = np.random.default_rng(41)
+    n, k, V = 24, 5, 70000
+    target, draft, toks, cu = synthetic(rng, n, k, V)
+    dt = torch.bfloat16
+    t, d = to_dev(target, dt), to_dev(draft, dt)
+    tk, cu_d = to_dev(toks), to_dev(cu)
+    ws = torch.full((sv.sv_verify_workspace_bytes(n, k),), 0x5a, dtype=torch.uint8, device="cuda")
+    for i, (mode, step) in enumerate([(sv.SV_STOCHASTIC, 3), (sv.SV_GREEDY, 0),
+                                      (sv.SV_STOCHASTIC, 4), (sv.SV_STOCHASTIC, 4)]):
+        got = sv.verify(t, d, tk, cu_d, mode, 0.9, 11, step, ws=ws)
+        want = sv.verify(t, d, tk, cu_d, mode, 0.9, 11, step)
+        torch.cuda.synchronize()
+        for key in want:
+            np.testing.assert_array_equal(got[key].cpu().numpy(), want[key].cpu().numpy(),
+                                          err_msg=f"call {i}: {key}")
