@@ -28,6 +28,12 @@ Parity pin status (what the oracle is checked against, in tests/):
 * budget_select — pinned by exhaustive exact-rational search over every
   per-request allocation on small cases, by the truncated-k table read as a
   cost model, and by prefix-closure invariants.
+* uniform_k_select — pinned by the FOS truncated-k table (tokens per computed
+  position is its goodput for one request whose step cost grows with the
+  positions computed), by exact-rational search, by equality with the budget
+  for a single request, by the budget's score bounding it, and by the DSD
+  page's claim that the chosen K falls as the batch grows into the compute
+  bound.
 * cost_table_prepare — pinned by the 121 -> 128 padding example on the
   agentlens page and by monotonicity.
 * pack_varlen — pinned by hand-derived golden fixtures and capacity formula.
@@ -52,6 +58,7 @@ from .budget import (
     DEV_BAD_DRAFT_LEN,
     DEV_BAD_COST,
 )
+from .uniform_k import uniform_k_select
 from .pack import pack_varlen, DEV_BAD_KEPT
 from .verify import (
     row_probs,
@@ -71,7 +78,7 @@ from .verify import (
 __all__ = [
     "philox4x32_10", "uniforms", "PHILOX_ROUNDS",
     "clamp_confidence", "survival", "cost_table_prepare", "rank_slots",
-    "fixed_point", "expected_tokens", "budget_score", "budget_select",
+    "fixed_point", "expected_tokens", "budget_score", "budget_select", "uniform_k_select",
     "pack_varlen", "row_probs", "accept", "residual_weights", "inverse_cdf",
     "row_is_faulty", "verify_request", "verify", "GREEDY", "STOCHASTIC",
     "DEV_BAD_DRAFT_LEN", "DEV_BAD_COST", "DEV_BAD_KEPT", "DEV_BAD_CU_ROWS",
