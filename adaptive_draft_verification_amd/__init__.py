@@ -27,7 +27,8 @@ SV_DEV_BAD_DRAFT_LEN, SV_DEV_BAD_COST, SV_DEV_BAD_KEPT = 8, 16, 32
 SV_MAX_BUDGET_SLOTS, SV_MAX_DRAFT, SV_MAX_VOCAB = 8192, 64, 1048576
 
 EXPORTED = ["sv_status_str", "sv_budget_workspace_bytes", "sv_verify_workspace_bytes",
-            "sv_cost_table_prepare", "sv_budget_select", "sv_pack_varlen", "sv_verify",
+            "sv_cost_table_prepare", "sv_budget_select", "sv_uniform_k_select", "sv_pack_varlen",
+            "sv_verify",
             "sv_verify_stages", "sv_philox_uniforms"]
 
 
@@ -52,6 +53,8 @@ def _load():
         "sv_cost_table_prepare": (ctypes.c_int, [vp, i32, i32, vp, i32]),
         "sv_budget_select": (ctypes.c_int, [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp,
                                             vp, sz, vp]),
+        "sv_uniform_k_select": (ctypes.c_int, [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp,
+                                               vp, vp]),
         "sv_pack_varlen": (ctypes.c_int, [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]),
         "sv_verify": (ctypes.c_int, [vp, i64, i64, vp, i64, ctypes.c_int, i32, vp, vp, i32, i32,
                                      ctypes.c_int, f32, u64, u64, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -144,6 +147,28 @@ def sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survi
                                  _ptr(survival), _ptr(dev_error), _ptr(ws), 0 if ws is None else ws.numel(),
                                  _stream(stream)),
            "sv_budget_select")
+
+
+def sv_uniform_k_select(conf, draft_len, cost, t_base, n_bonus, kept, k_out, scores=None,
+                        dev_error=None, stream=None):
+    """conf [n, k_max] f32, draft_len [n] i32, cost [L] f32 -> kept [n] i32, k_out [1] i32,
+    scores [k_max + 1] f64 (optional)."""
+    _dev(conf, torch.float32, "conf", 2)
+    _dev(draft_len, torch.int32, "draft_len", 1)
+    _dev(cost, torch.float32, "cost", 1)
+    _dev(kept, torch.int32, "kept", 1)
+    _dev(k_out, torch.int32, "k_out", 1)
+    _dev(scores, torch.float64, "scores", 1)
+    _dev(dev_error, torch.int32, "dev_error", 1)
+    n, k_max = conf.shape
+    if draft_len.numel() != n or kept.numel() != n or k_out.numel() < 1:
+        raise ValueError("draft_len, kept must have n entries and k_out one")
+    if scores is not None and scores.numel() != k_max + 1:
+        raise ValueError("scores must have k_max + 1 entries")
+    _check(_lib.sv_uniform_k_select(_ptr(conf), _ptr(draft_len), n, k_max, _ptr(cost),
+                                    cost.numel(), int(t_base), int(n_bonus), _ptr(kept),
+                                    _ptr(k_out), _ptr(scores), _ptr(dev_error), _stream(stream)),
+           "sv_uniform_k_select")
 
 
 def sv_pack_varlen(kept, last_token, draft_tokens, cu_rows, row_req, row_pos, packed_tokens,
@@ -253,6 +278,18 @@ def budget_select(conf, draft_len, cost, t_base, n_bonus, stream=None):
     sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survival, err, stream,
                      ws=ws)
     return dict(kept=kept, budget=budget, survival=survival, dev_error=err)
+
+
+def uniform_k_select(conf, draft_len, cost, t_base, n_bonus, stream=None):
+    dev = conf.device
+    n, k_max = conf.shape
+    out = dict(kept=torch.empty(n, dtype=torch.int32, device=dev),
+               k=torch.empty(1, dtype=torch.int32, device=dev),
+               scores=torch.empty(k_max + 1, dtype=torch.float64, device=dev),
+               dev_error=torch.zeros(1, dtype=torch.int32, device=dev))
+    sv_uniform_k_select(conf, draft_len, cost, t_base, n_bonus, out["kept"], out["k"],
+                        out["scores"], out["dev_error"], stream)
+    return out
 
 
 def pack_varlen(kept, last_token, draft_tokens, stream=None):

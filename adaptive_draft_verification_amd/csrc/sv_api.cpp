@@ -86,6 +86,23 @@ sv_status sv_budget_select(const float* conf, const int32_t* draft_len, int32_t 
                                       budget, survival, dev_error, ws, as_stream(stream)));
 }
 
+sv_status sv_uniform_k_select(const float* conf, const int32_t* draft_len, int32_t n_req,
+                              int32_t k_max, const float* cost, int32_t cost_len, int32_t t_base,
+                              int32_t n_bonus, int32_t* kept, int32_t* k_out, double* scores,
+                              int32_t* dev_error, void* stream) {
+    if (n_req < 0 || k_max < 0) return SV_ERR_SHAPE;
+    if (cost == nullptr || k_out == nullptr) return SV_ERR_NULL;
+    if (n_req > 0 && (draft_len == nullptr || kept == nullptr)) return SV_ERR_NULL;
+    if (n_req > 0 && k_max > 0 && conf == nullptr) return SV_ERR_NULL;
+    if (n_req > SV_MAX_BUDGET_SLOTS || k_max > SV_MAX_DRAFT ||
+        (int64_t)n_req * k_max > SV_MAX_BUDGET_SLOTS)
+        return SV_ERR_SHAPE;
+    if (t_base < 0 || n_bonus < 0) return SV_ERR_VALUE;
+    if ((int64_t)cost_len < (int64_t)t_base + (int64_t)n_req * k_max + 1) return SV_ERR_SHAPE;
+    return launched(sv::launch_uniform_k(conf, draft_len, n_req, k_max, cost, t_base, n_bonus,
+                                         kept, k_out, scores, dev_error, as_stream(stream)));
+}
+
 sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
                          const int32_t* draft_tokens, int32_t n_req, int32_t k_max,
                          int32_t* cu_rows, int32_t* row_req, int32_t* row_pos,

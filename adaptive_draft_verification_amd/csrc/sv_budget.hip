@@ -312,6 +312,110 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     }
 }
 
+// One draft length for the whole batch ("Hardware-Aware Dynamic Speculative
+// Decoding (DSD), feat. Cohere", section "동적 추측 디코딩(DSD)의 핵심
+// 아이디어": K chosen by goodput = acceptance length / step latency).  One
+// workgroup: confidences staged in LDS, one thread per request forms its
+// survival chain and adds floor(s * 2^40) of position j into column j (LDS
+// integer atomics: exact, order free); thread K forms
+// S(K) = sum of columns j < K and T(K) = drafts verified at K, and the score
+// (n_bonus + S * 2^-40) / cost[t_base + T] in IEEE fp64; the first maximiser
+// is K*, and kept[r] = min(K*, K_r).
+__global__ __launch_bounds__(kThreads) void uniform_k_kernel(
+    const float* __restrict__ conf, const int32_t* __restrict__ draft_len, int n_req, int k_max,
+    const float* __restrict__ cost, int t_base, int n_bonus, int32_t* __restrict__ kept,
+    int32_t* __restrict__ k_out, double* __restrict__ scores, int32_t* dev_error) {
+    __shared__ float conf_s[kConfLds];
+    __shared__ unsigned long long col_sum[SV_MAX_DRAFT];
+    __shared__ int32_t col_cnt[SV_MAX_DRAFT];
+    __shared__ double score_s[SV_MAX_DRAFT + 1];
+    __shared__ int32_t err_s, best_s;
+
+    const int tid = threadIdx.x;
+    const int n_slots = n_req * k_max;
+    const int kp = k_max | 1;
+    float c[kPerThread];
+    int32_t dl[kPerThread];
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int x = tid + q * kThreads;
+        c[q] = x < n_slots ? conf[x] : 0.0f;
+        dl[q] = x < n_req ? draft_len[x] : 0;
+    }
+    if (tid < SV_MAX_DRAFT) {
+        col_sum[tid] = 0ull;
+        col_cnt[tid] = 0;
+    }
+    if (tid == 0) err_s = 0;
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int x = tid + q * kThreads;
+        if (x < n_slots) {
+            const int r = x / k_max;
+            conf_s[r * kp + (x - r * k_max)] = clamp_confidence(c[q]);
+        }
+    }
+    __syncthreads();
+
+    int my_err = 0;
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int r = tid + q * kThreads;
+        if (r < n_req) {
+            const int K = clamp_len(dl[q], k_max);
+            if (K != dl[q]) my_err |= SV_DEV_BAD_DRAFT_LEN;
+            float sv = 1.0f;
+            for (int j = 0; j < K; ++j) {
+                sv = __fmul_rn(sv, conf_s[r * kp + j]);
+                // s * 2^40 is exact in fp32; the conversion truncates = floor
+                atomicAdd(&col_sum[j], (unsigned long long)(sv * 0x1p40f));
+                atomicAdd(&col_cnt[j], 1);
+            }
+        }
+    }
+    if (my_err) atomicOr(&err_s, my_err);
+    __syncthreads();
+
+    if (tid <= k_max) {
+        const int K = tid;
+        unsigned long long S = 0ull;
+        int T = 0;
+        for (int j = 0; j < K; ++j) {
+            S += col_sum[j];
+            T += col_cnt[j];
+        }
+        const float cst = cost[t_base + T];
+        double sc = -__builtin_inf();
+        if (cst > 0.0f && is_finite_bits(cst)) {
+            // S < 2^53 and 2^-40 is a power of two: the product is exact
+            sc = ((double)n_bonus + (double)S * 0x1p-40) / (double)cst;
+        } else {
+            atomicOr(&err_s, SV_DEV_BAD_COST);
+        }
+        score_s[K] = sc;
+        if (scores != nullptr) scores[K] = sc;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int best = 0;
+        for (int K = 1; K <= k_max; ++K)
+            if (score_s[K] > score_s[best]) best = K;  // the first maximiser
+        best_s = best;
+        k_out[0] = best;
+        raise_error(dev_error, err_s);
+    }
+    __syncthreads();
+    const int best = best_s;
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int r = tid + q * kThreads;
+        if (r < n_req) {
+            const int K = clamp_len(dl[q], k_max);
+            kept[r] = K < best ? K : best;
+        }
+    }
+}
+
 }  // namespace
 
 size_t budget_workspace_bytes(int n_req, int k_max) {
@@ -333,6 +437,19 @@ hipError_t launch_budget(const float* conf, const int32_t* draft_len, int n_req,
     }
     hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kThreads), 0, stream, n_req, k_max, cost,
                        t_base, n_bonus, kept, budget, dev_error, ws);
+    return hipGetLastError();
+}
+
+}  // namespace sv
+
+namespace sv {
+
+hipError_t launch_uniform_k(const float* conf, const int32_t* draft_len, int n_req, int k_max,
+                            const float* cost, int t_base, int n_bonus, int32_t* kept,
+                            int32_t* k_out, double* scores, int32_t* dev_error,
+                            hipStream_t stream) {
+    hipLaunchKernelGGL(uniform_k_kernel, dim3(1), dim3(kThreads), 0, stream, conf, draft_len,
+                       n_req, k_max, cost, t_base, n_bonus, kept, k_out, scores, dev_error);
     return hipGetLastError();
 }
 

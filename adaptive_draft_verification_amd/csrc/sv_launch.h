@@ -16,6 +16,11 @@ hipError_t launch_budget(const float* conf, const int32_t* draft_len, int n_req,
                          hipStream_t stream);
 size_t budget_workspace_bytes(int n_req, int k_max);
 
+hipError_t launch_uniform_k(const float* conf, const int32_t* draft_len, int n_req, int k_max,
+                            const float* cost, int t_base, int n_bonus, int32_t* kept,
+                            int32_t* k_out, double* scores, int32_t* dev_error,
+                            hipStream_t stream);
+
 hipError_t launch_pack(const int32_t* kept, const int32_t* last_token,
                        const int32_t* draft_tokens, int n_req, int k_max, int32_t* cu_rows,
                        int32_t* row_req, int32_t* row_pos, int32_t* packed_tokens,

@@ -348,6 +348,23 @@ def main():
             "iters": args.full_k_iters,
         }
 
+    # ------------------------------------------------ uniform draft length leg
+    # the DSD-style alternative to the adaptive budget: one K for the batch
+    uk_k = torch.empty(1, dtype=torch.int32, device=dev)
+    uk_kept = torch.empty(n, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        sv.sv_uniform_k_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, uk_kept, uk_k, None,
+                               err)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        sv.sv_uniform_k_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, uk_kept, uk_k, None,
+                               err)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    uniform_k = {"us": round(e0.elapsed_time(e1) / args.steps * 1e3, 2), "k": int(uk_k.item()),
+                 "drafts_verified": int(uk_kept.sum().item())}
+
     # ------------------------------------------------------------ CPU oracle leg
     cpu = None
     if not args.no_cpu_baseline:
@@ -405,6 +422,7 @@ def main():
         "launch": "hip-graph replay" if graphs else "eager",
         "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 4),
         "step_hbm_gbps": round((pass1_bytes + pass2_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
+        "uniform_k": uniform_k,
         "full_k": full,
         "cpu_baseline": cpu,
     }

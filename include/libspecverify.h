@@ -145,6 +145,37 @@ sv_status sv_budget_select(const float* conf, const int32_t* draft_len, int32_t 
                            int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sv_uniform_k_select — one draft length K for the whole batch, by goodput.
+ *
+ * "Hardware-Aware Dynamic Speculative Decoding (DSD), feat. Cohere", section
+ * "동적 추측 디코딩(DSD)의 핵심 아이디어": the number of drafts is chosen per
+ * step from the model/hardware interaction by maximising goodput =
+ * acceptance length / inter-token latency (more drafts while memory-bound,
+ * fewer once compute-bound).  Here, with the survivals s of
+ * sv_budget_select (same clamping, fp32 products):
+ *   K* = the smallest maximiser over K = 0 .. k_max of
+ *        (n_bonus + S(K)) / cost[t_base + T(K)],
+ *   S(K) = sum over r of the survivals of r's first min(K, K_r) drafts, taken
+ *          exactly as sum(floor(s * 2^40)) * 2^-40, the ratio in fp64;
+ *   T(K) = sum over r of min(K, K_r) (drafts verified);
+ *   kept[r] = min(K*, K_r).
+ * The acceptance length is the FOS page's (section "평균 수락 길이"): one
+ * plus the survivals of the drafts verified.
+ *
+ * conf, draft_len, cost, t_base, n_bonus: as for sv_budget_select.
+ * kept:    [n_req] int32 out.   k_out: [1] int32 out (K*).
+ * scores:  [k_max + 1] fp64 out (the goodput of every K; -inf where the cost
+ *          entry is unusable), or NULL.
+ * Launch: one workgroup of 1024 threads; no workspace.
+ * Errors: as for sv_budget_select (SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_VALUE);
+ * device bits SV_DEV_BAD_DRAFT_LEN, SV_DEV_BAD_COST.
+ */
+sv_status sv_uniform_k_select(const float* conf, const int32_t* draft_len, int32_t n_req,
+                              int32_t k_max, const float* cost, int32_t cost_len, int32_t t_base,
+                              int32_t n_bonus, int32_t* kept, int32_t* k_out, double* scores,
+                              int32_t* dev_error, void* stream);
+
+/*
  * sv_pack_varlen — lay the kept rows out as one varlen decode batch.
  *
  * agentlens page, section "기술적 구현 및 CUDA Graphs", item Graph Capture:

@@ -72,6 +72,20 @@ def check_budget(conf, draft_len, k_max, cost, t_base, n_bonus):
     return o
 
 
+def check_uniform_k(conf, draft_len, k_max, cost, t_base, n_bonus):
+    """Uniform draft length: K*, kept counts and every K's fp64 score exact."""
+    conf = np.asarray(conf, np.float32).reshape(len(draft_len), k_max)
+    g = sv.uniform_k_select(to_dev(conf), to_dev(np.asarray(draft_len, np.int32)),
+                            to_dev(np.asarray(cost, np.float32)), t_base, n_bonus)
+    torch.cuda.synchronize()
+    o = oracle.uniform_k_select(conf, draft_len, k_max, cost, t_base, n_bonus)
+    assert int(g["k"].cpu()[0]) == o["k"], (int(g["k"].cpu()[0]), o["k"])
+    np.testing.assert_array_equal(g["kept"].cpu().numpy(), o["kept"])
+    np.testing.assert_array_equal(g["scores"].cpu().numpy(), np.array(o["scores"], np.float64))
+    assert int(g["dev_error"].cpu()[0]) == o["dev_error"]
+    return o
+
+
 # -------------------------------------------------------------------- pack
 
 def check_pack(kept, last_token, draft_tokens, k_max):

@@ -109,6 +109,27 @@ def test_budget_select_host_validation():
     assert budget(ws=FAKE, ws_bytes=need - 1) == sv.SV_ERR_WORKSPACE
 
 
+def uniform_k(**kw):
+    args = dict(conf=FAKE, draft_len=FAKE, n_req=4, k_max=3, cost=FAKE, cost_len=17, t_base=4,
+                n_bonus=4, kept=FAKE, k_out=FAKE, scores=None, dev_error=None, stream=None)
+    args.update(kw)
+    return sv._lib.sv_uniform_k_select(*args.values())
+
+
+def test_uniform_k_host_validation():
+    assert uniform_k(cost_len=16) == sv.SV_ERR_SHAPE          # needs t_base + n*k + 1
+    assert uniform_k(n_req=-1) == sv.SV_ERR_SHAPE
+    assert uniform_k(k_max=65, cost_len=300) == sv.SV_ERR_SHAPE
+    assert uniform_k(n_req=2048, k_max=5, cost_len=20000) == sv.SV_ERR_SHAPE
+    assert uniform_k(t_base=-1) == sv.SV_ERR_VALUE
+    assert uniform_k(n_bonus=-1) == sv.SV_ERR_VALUE
+    for key in ("conf", "draft_len", "cost", "kept", "k_out"):
+        assert uniform_k(**{key: None}) == sv.SV_ERR_NULL, key
+    # no requests: nothing needs the request arrays
+    assert uniform_k(n_req=0, conf=None, draft_len=None, kept=None, cost_len=5,
+                     k_out=None) == sv.SV_ERR_NULL  # k_out is always written
+
+
 def pack(**kw):
     args = dict(kept=FAKE, last_token=FAKE, draft_tokens=FAKE, n_req=4, k_max=3, cu_rows=FAKE,
                 row_req=FAKE, row_pos=FAKE, packed=FAKE, dev_error=None, stream=None)

@@ -14,8 +14,8 @@ import torch
 import oracle
 import workloads
 
-from parity import (check_budget, check_pack, compare_verify, gpu_verify, logits_dtype, to_dev,
-                    workload_inputs)
+from parity import (check_budget, check_pack, check_uniform_k, compare_verify, gpu_verify,
+                    logits_dtype, to_dev, workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +95,45 @@ def test_budget_denormal_survivals():
     dl = np.full(4, 6, dtype=np.int32)
     cost = np.ones(4 + 24 + 1, dtype=np.float32)
     check_budget(conf, dl, 6, cost, 4, 4)
+
+
+# ------------------------------------------------------- uniform draft length
+
+@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
+def test_uniform_k_workloads(name):
+    w = workloads.make(name)
+    cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+    o = check_uniform_k(w.conf, w.draft_len, w.k_max, cost, w.t_base, w.n_bonus)
+    log(f"{name}: K*={o['k']}")
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_uniform_k_random(seed):
+    rng = np.random.default_rng(500 + seed)
+    n = int(rng.integers(1, 300))
+    k = int(rng.integers(1, min(16, 8192 // n) + 1))
+    conf, dl, cost, t_base, n_bonus = workloads.random_budget_case(
+        rng, n, k, ties=seed % 2 == 0, zeros=seed % 3 == 0, flat_cost=seed % 7 == 0)
+    if seed % 5 == 0:
+        cost = np.maximum.accumulate(cost)
+    if seed % 11 == 0:
+        dl[0] = k + 3
+        dl[-1] = -2
+        conf[0, 0] = np.nan
+    if seed % 13 == 0:
+        cost[t_base + 1] = np.nan
+    check_uniform_k(conf, dl, k, cost, t_base, n_bonus)
+
+
+@pytest.mark.parametrize("n,k", [(8192, 1), (1024, 8), (128, 64), (1, 64), (1, 1), (3, 0),
+                                 (0, 4)])
+def test_uniform_k_edges(n, k):
+    rng = np.random.default_rng(n + 3 * k)
+    conf = rng.uniform(0.3, 1.0, (n, k)).astype(np.float32)
+    dl = rng.integers(0, k + 1, n).astype(np.int32)
+    t = np.arange(n + n * k + 1, dtype=np.float32)
+    cost = np.maximum(1.0, t / max(1, n)).astype(np.float32)
+    check_uniform_k(conf, dl, k, cost, n, n)
 
 
 # -------------------------------------------------------------------- pack
