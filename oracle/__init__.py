@@ -34,6 +34,12 @@ Parity pin status (what the oracle is checked against, in tests/):
   for a single request, by the budget's score bounding it, and by the DSD
   page's claim that the chosen K falls as the batch grows into the compute
   bound.
+* accept_stats — pinned by a hand-derived case and by the FOS per-position
+  table (conditional column = accepted / verified, cumulative = running
+  product, mean acceptance length = 1 + sum of the cumulative column).
+* calibrate_update / calibrate_predict — pinned by finite differences of an
+  independently written log-loss, by the gradient vanishing (in mean) at the
+  parameters that generated the outcomes, and by the sign of an update.
 * cost_table_prepare — pinned by the 121 -> 128 padding example on the
   agentlens page and by monotonicity.
 * pack_varlen — pinned by hand-derived golden fixtures and capacity formula.
@@ -59,6 +65,7 @@ from .budget import (
     DEV_BAD_COST,
 )
 from .uniform_k import uniform_k_select
+from .calibrate import accept_stats, calibrate_update, predict as calibrate_predict
 from .pack import pack_varlen, DEV_BAD_KEPT
 from .verify import (
     row_probs,
@@ -79,6 +86,7 @@ __all__ = [
     "philox4x32_10", "uniforms", "PHILOX_ROUNDS",
     "clamp_confidence", "survival", "cost_table_prepare", "rank_slots",
     "fixed_point", "expected_tokens", "budget_score", "budget_select", "uniform_k_select",
+    "accept_stats", "calibrate_update", "calibrate_predict",
     "pack_varlen", "row_probs", "accept", "residual_weights", "inverse_cdf",
     "row_is_faulty", "verify_request", "verify", "GREEDY", "STOCHASTIC",
     "DEV_BAD_DRAFT_LEN", "DEV_BAD_COST", "DEV_BAD_KEPT", "DEV_BAD_CU_ROWS",

@@ -1,0 +1,118 @@
+"""Pins of the oracle's acceptance statistics and logistic calibration: a
+hand-derived case, the FOS per-position table, finite differences of the
+log-loss, unbiasedness of the gradient at the generating parameters, and the
+direction of an update."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.calibrate as cal
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def cu_from_kept(kept):
+    return np.concatenate([[0], np.cumsum(np.asarray(kept) + 1)]).astype(np.int32)
+
+
+def test_hand_case():
+    # r0 keeps 3, accepts 1 (verifies 0 ok, 1 rejected); r1 keeps 2, accepts both;
+    # r2 keeps 0 (bonus only); r3 faulted (-1) and counts for nothing
+    kept = [3, 2, 0, 4]
+    res = cal.accept_stats([1, 2, 0, -1], cu_from_kept(kept), 4)
+    assert res["attempted"].tolist() == [2, 2, 0, 0]
+    assert res["accepted_at"].tolist() == [2, 1, 0, 0]
+    assert res["requests"] == 3 and res["emitted"] == 2 + 3 + 1
+
+
+def test_fos_per_position_table():
+    """FOS per-position table: the conditional column is accepted_j / attempted_j
+    and the cumulative column is accepted_j / requests; their running product
+    agrees, and the mean acceptance length is 1 + the sum of the cumulative
+    column (section "평균 수락 길이": 1.93 at k = 7)."""
+    g = json.load(open(os.path.join(GOLDEN, "fos_truncated_k_table.json")))
+    cum = g["cumulative_acceptance"]
+    n, k = 100000, 7
+    # requests accepting at least j+1 drafts: n * cum[j]
+    at_least = [n] + [round(n * c) for c in cum]
+    L = []
+    for j in range(k + 1):
+        count = at_least[j] - (at_least[j + 1] if j < k else 0)
+        L += [j] * count
+    res = cal.accept_stats(np.array(L), cu_from_kept([k] * len(L)), k)
+    cond = res["accepted_at"] / res["attempted"]
+    prod = np.cumprod(cond)
+    np.testing.assert_allclose(prod, np.array(cum), atol=1e-5)
+    np.testing.assert_allclose(res["accepted_at"] / res["requests"], cum, atol=1e-5)
+    assert res["emitted"] / res["requests"] == pytest.approx(1 + sum(cum), abs=1e-4)
+    assert res["emitted"] / res["requests"] == pytest.approx(g["rows"][7]["mean_acceptance_length"],
+                                                             abs=0.006)
+
+
+def synthetic(rng, n, k, theta):
+    """Draft probabilities and outcomes drawn from the logistic model theta:
+    a request stops at its first rejection (the verify rule)."""
+    kept = rng.integers(0, k + 1, n)
+    q = np.where(rng.uniform(size=(n, k)) < 0.05, 0.0, rng.uniform(0.01, 1.0, (n, k)))
+    L = np.zeros(n, dtype=np.int64)
+    for r in range(n):
+        j = 0
+        while j < kept[r]:
+            p = cal.sigmoid(theta[j] + theta[k] * cal.feature(q[r, j]))
+            if rng.uniform() >= p:
+                break
+            j += 1
+        L[r] = j
+    return q, L, cu_from_kept(kept)
+
+
+def test_gradient_matches_finite_differences():
+    rng = np.random.default_rng(3)
+    k = 4
+    theta = rng.normal(0, 1, k + 1)
+    q, L, cu = synthetic(rng, 300, k, rng.normal(0, 1, k + 1))
+    g, count = cal.gradient(theta, q, L, cu, k)
+    assert count > 0
+    h = 1e-6
+    for i in range(k + 1):
+        tp, tm = theta.copy(), theta.copy()
+        tp[i] += h
+        tm[i] -= h
+        fd = (cal.log_loss(tp, q, L, cu, k) - cal.log_loss(tm, q, L, cu, k)) / (2 * h)
+        assert g[i] == pytest.approx(fd, rel=1e-5, abs=1e-6), i
+
+
+def test_gradient_is_unbiased_at_the_generating_parameters():
+    """With outcomes drawn from theta*, the mean gradient at theta* is ~0 and
+    clearly not ~0 at a shifted theta."""
+    rng = np.random.default_rng(5)
+    k = 3
+    star = np.array([1.2, 0.4, -0.3, 0.25])
+    q, L, cu = synthetic(rng, 40000, k, star)
+    g, count = cal.gradient(star, q, L, cu, k)
+    assert np.all(np.abs(g / count) < 0.01), g / count
+    off = star + np.array([0.5, -0.5, 0.5, 0.1])
+    g2, _ = cal.gradient(off, q, L, cu, k)
+    assert np.max(np.abs(g2 / count)) > 0.03
+
+
+def test_update_moves_toward_the_outcomes():
+    k = 2
+    theta = np.zeros(k + 1)
+    q = np.full((4, k), 0.5)
+    all_acc, _ = cal.calibrate_update(theta, q, [2, 2, 2, 2], cu_from_kept([2] * 4), k, 1.0)
+    all_rej, _ = cal.calibrate_update(theta, q, [0, 0, 0, 0], cu_from_kept([2] * 4), k, 1.0)
+    assert all_acc[0] > 0 and all_acc[1] > 0
+    assert all_rej[0] < 0 and all_rej[1] == 0  # position 1 never verified
+
+
+def test_predict_and_feature():
+    assert cal.feature(0.0) == -64 and cal.feature(1.0) == 0 and cal.feature(0.25) == -2
+    assert cal.feature(float("nan")) == -64 and cal.feature(2.0) == 0
+    c = cal.predict(np.array([0.0, math.log(3.0), 1.0]), np.array([[1.0, 0.5]]), 2)
+    assert c[0, 0] == pytest.approx(0.5)
+    assert c[0, 1] == pytest.approx(cal.sigmoid(math.log(3.0) - 1.0))
