@@ -29,7 +29,8 @@ SV_MAX_BUDGET_SLOTS, SV_MAX_DRAFT, SV_MAX_VOCAB = 8192, 64, 1048576
 EXPORTED = ["sv_status_str", "sv_budget_workspace_bytes", "sv_verify_workspace_bytes",
             "sv_cost_table_prepare", "sv_budget_select", "sv_uniform_k_select", "sv_pack_varlen",
             "sv_verify",
-            "sv_verify_stages", "sv_philox_uniforms"]
+            "sv_verify_stages", "sv_accept_stats", "sv_calibrate_update", "sv_calibrate_predict",
+            "sv_philox_uniforms"]
 
 
 class SvError(RuntimeError):
@@ -62,6 +63,9 @@ def _load():
         "sv_verify_stages": (ctypes.c_int, [vp, i64, i64, vp, i64, ctypes.c_int, i32, vp, vp, i32,
                                             i32, ctypes.c_int, f32, u64, u64, vp, vp, vp, vp, vp,
                                             vp, vp, sz, i32, vp]),
+        "sv_accept_stats": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp, vp]),
+        "sv_calibrate_update": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, f32, vp, vp]),
+        "sv_calibrate_predict": (ctypes.c_int, [vp, vp, i32, i32, vp, vp]),
         "sv_philox_uniforms": (ctypes.c_int, [u64, u64, i32, i32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -250,6 +254,50 @@ def sv_verify_stages(target, draft, draft_tokens, cu_rows, mode, temperature, se
                         out_tokens, out_accepted, ws, out_p_draft, out_q_draft,
                         out_residual_mass, dev_error, vocab)
     _check(_lib.sv_verify_stages(*args, int(stages), _stream(stream)), "sv_verify_stages")
+
+
+def sv_accept_stats(accepted, cu_rows, attempted, accepted_at, totals, stream=None):
+    """accepted [n] i32, cu_rows [n+1] i32 -> adds to attempted/accepted_at [k_max] and
+    totals [2] (int64 device tensors holding uint64 counts)."""
+    _dev(accepted, torch.int32, "accepted", 1)
+    _dev(cu_rows, torch.int32, "cu_rows", 1)
+    for name, t in (("attempted", attempted), ("accepted_at", accepted_at), ("totals", totals)):
+        _dev(t, torch.int64, name, 1)
+    n = accepted.numel()
+    k_max = attempted.numel()
+    if cu_rows.numel() != n + 1 or accepted_at.numel() != k_max or totals.numel() < 2:
+        raise ValueError("cu_rows [n+1], attempted/accepted_at [k_max], totals [2]")
+    _check(_lib.sv_accept_stats(_ptr(accepted), _ptr(cu_rows), n, k_max, _ptr(attempted),
+                                _ptr(accepted_at), _ptr(totals), _stream(stream)),
+           "sv_accept_stats")
+
+
+def sv_calibrate_update(theta, q_draft, accepted, cu_rows, lr, count_out=None, stream=None):
+    """theta [k_max+1] f32 (in place), q_draft [n, k_max] f32, accepted [n], cu_rows [n+1]."""
+    _dev(theta, torch.float32, "theta", 1)
+    _dev(q_draft, torch.float32, "q_draft", 2)
+    _dev(accepted, torch.int32, "accepted", 1)
+    _dev(cu_rows, torch.int32, "cu_rows", 1)
+    _dev(count_out, torch.int32, "count_out", 1)
+    n, k_max = q_draft.shape
+    if theta.numel() != k_max + 1 or accepted.numel() != n or cu_rows.numel() != n + 1:
+        raise ValueError("theta [k_max+1], accepted [n], cu_rows [n+1]")
+    _check(_lib.sv_calibrate_update(_ptr(theta), _ptr(q_draft), _ptr(accepted), _ptr(cu_rows), n,
+                                    k_max, float(lr), _ptr(count_out), _stream(stream)),
+           "sv_calibrate_update")
+
+
+def sv_calibrate_predict(theta, q_draft, conf, stream=None):
+    """conf [n, k_max] f32 <- sigmoid(alpha_j + beta * log2 q)."""
+    _dev(theta, torch.float32, "theta", 1)
+    _dev(q_draft, torch.float32, "q_draft", 2)
+    _dev(conf, torch.float32, "conf", 2)
+    n, k_max = q_draft.shape
+    if theta.numel() != k_max + 1 or tuple(conf.shape) != (n, k_max):
+        raise ValueError("theta [k_max+1], conf [n, k_max]")
+    _check(_lib.sv_calibrate_predict(_ptr(theta), _ptr(q_draft), n, k_max, _ptr(conf),
+                                     _stream(stream)),
+           "sv_calibrate_predict")
 
 
 def sv_philox_uniforms(seed, step, u, v, stream=None):

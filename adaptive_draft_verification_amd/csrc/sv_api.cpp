@@ -168,6 +168,38 @@ sv_status sv_verify(const void* target_logits, int64_t target_ld, int64_t target
                             out_residual_mass, dev_error, ws, ws_bytes, 3, stream);
 }
 
+sv_status sv_accept_stats(const int32_t* accepted, const int32_t* cu_rows, int32_t n_req,
+                          int32_t k_max, uint64_t* attempted, uint64_t* accepted_at,
+                          uint64_t* totals, void* stream) {
+    if (n_req < 0 || k_max < 0 || k_max > SV_MAX_DRAFT) return SV_ERR_SHAPE;
+    if (totals == nullptr || (k_max > 0 && (attempted == nullptr || accepted_at == nullptr)))
+        return SV_ERR_NULL;
+    if (n_req > 0 && (accepted == nullptr || cu_rows == nullptr)) return SV_ERR_NULL;
+    return launched(sv::launch_accept_stats(accepted, cu_rows, n_req, k_max, attempted,
+                                            accepted_at, totals, as_stream(stream)));
+}
+
+sv_status sv_calibrate_update(float* theta, const float* q_draft, const int32_t* accepted,
+                              const int32_t* cu_rows, int32_t n_req, int32_t k_max, float lr,
+                              int32_t* count_out, void* stream) {
+    if (n_req < 0 || k_max < 0 || k_max > SV_MAX_DRAFT) return SV_ERR_SHAPE;
+    if (!std::isfinite(lr) || lr < 0.0f) return SV_ERR_VALUE;
+    if (theta == nullptr) return SV_ERR_NULL;
+    if (n_req > 0 && (accepted == nullptr || cu_rows == nullptr)) return SV_ERR_NULL;
+    if (n_req > 0 && k_max > 0 && q_draft == nullptr) return SV_ERR_NULL;
+    return launched(sv::launch_calibrate_update(theta, q_draft, accepted, cu_rows, n_req, k_max,
+                                                lr, count_out, as_stream(stream)));
+}
+
+sv_status sv_calibrate_predict(const float* theta, const float* q_draft, int32_t n_req,
+                               int32_t k_max, float* conf, void* stream) {
+    if (n_req < 0 || k_max < 0 || k_max > SV_MAX_DRAFT) return SV_ERR_SHAPE;
+    if ((int64_t)n_req * k_max > 0 && (theta == nullptr || q_draft == nullptr || conf == nullptr))
+        return SV_ERR_NULL;
+    return launched(sv::launch_calibrate_predict(theta, q_draft, n_req, k_max, conf,
+                                                 as_stream(stream)));
+}
+
 sv_status sv_philox_uniforms(uint64_t seed, uint64_t step, int32_t n_req, int32_t n_pos,
                              float* u, float* v, void* stream) {
     if (n_req < 0 || n_pos < 0) return SV_ERR_SHAPE;

@@ -55,6 +55,15 @@ struct VerifyArgs {
 size_t verify_workspace_bytes(int n_req, int k_max);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 
+hipError_t launch_accept_stats(const int32_t* accepted, const int32_t* cu_rows, int n_req,
+                               int k_max, uint64_t* attempted, uint64_t* accepted_at,
+                               uint64_t* totals, hipStream_t stream);
+hipError_t launch_calibrate_update(float* theta, const float* q_draft, const int32_t* accepted,
+                                   const int32_t* cu_rows, int n_req, int k_max, float lr,
+                                   int32_t* count_out, hipStream_t stream);
+hipError_t launch_calibrate_predict(const float* theta, const float* q_draft, int n_req,
+                                    int k_max, float* conf, hipStream_t stream);
+
 hipError_t launch_philox_uniforms(uint64_t seed, uint64_t step, int n_req, int n_pos, float* u,
                                   float* v, hipStream_t stream);
 

@@ -283,6 +283,59 @@ sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t
                            size_t ws_bytes, int32_t stages, void* stream);
 
 /*
+ * Acceptance statistics and online calibration of the per-position
+ * acceptance estimates.  FOS page, section "켜는 방법과 제약" (for model-based
+ * drafters without a confidence head, a small logistic model predicts
+ * acceptance from the draft's logits and is recalibrated while serving from
+ * the verification results), the measurement checklist (per-position
+ * acceptance rate and mean acceptance length) and section "평균 수락 길이".
+ *
+ * Outcomes come from sv_verify: request r kept b_r = cu_rows[r+1] - cu_rows[r]
+ * - 1 drafts and accepted L_r = accepted[r]; it verified positions
+ * 0 .. min(L_r, b_r - 1), accepting those below L_r and rejecting L_r when
+ * L_r < b_r.  Requests with L_r < 0 (a fault) or outside
+ * 0 <= L_r <= b_r <= k_max are skipped.
+ */
+
+/*
+ * sv_accept_stats — add one step's counters to running totals (device
+ * uint64, caller-owned, never cleared by the library).
+ * attempted[j] += requests that verified position j; accepted_at[j] += those
+ * that accepted it ([k_max] each: accepted_at/attempted is position j's
+ * conditional acceptance); totals[0] += requests counted, totals[1] += their
+ * emitted tokens sum(L_r + 1) (totals[1] / totals[0] = mean acceptance
+ * length).  One workgroup.  Errors: SV_ERR_SHAPE (n_req < 0, k_max outside
+ * [0, SV_MAX_DRAFT]), SV_ERR_NULL.
+ */
+sv_status sv_accept_stats(const int32_t* accepted, const int32_t* cu_rows, int32_t n_req,
+                          int32_t k_max, uint64_t* attempted, uint64_t* accepted_at,
+                          uint64_t* totals, void* stream);
+
+/*
+ * sv_calibrate_update — one gradient step of the logistic acceptance model
+ *   c_j = sigmoid(alpha_j + beta * x),  x = log2 q(d_j) clamped to [-64, 0]
+ * (q <= 0 or NaN reads as -64), theta = [alpha_0 .. alpha_{k_max-1}, beta]
+ * (device fp32 [k_max + 1], updated in place), on the mean log-loss of the
+ * verified positions: theta -= lr * grad / N.  q_draft: [n_req, k_max] fp32,
+ * sv_verify's out_q_draft.  count_out: [1] int32, N (or NULL).  One
+ * workgroup; fixed-order reductions (deterministic).  Errors: SV_ERR_SHAPE,
+ * SV_ERR_NULL, SV_ERR_VALUE (lr negative or not finite).
+ */
+sv_status sv_calibrate_update(float* theta, const float* q_draft, const int32_t* accepted,
+                              const int32_t* cu_rows, int32_t n_req, int32_t k_max, float lr,
+                              int32_t* count_out, void* stream);
+
+/*
+ * sv_calibrate_predict — conf[r, j] = sigmoid(alpha_j + beta * x(q[r, j])):
+ * the per-position acceptance estimates sv_budget_select and
+ * sv_uniform_k_select read, from the drafter's probabilities of its own
+ * tokens.  q_draft, conf: [n_req, k_max] fp32.  Errors: SV_ERR_SHAPE,
+ * SV_ERR_NULL.
+ */
+sv_status sv_calibrate_predict(const float* theta, const float* q_draft, int32_t n_req,
+                               int32_t k_max, float* conf, void* stream);
+
+/*
  * sv_philox_uniforms — the (u, v) pairs sv_verify draws, for inspection.
  * u, v: [n_req, n_pos] fp32 out for counters (r, j, step) with r < n_req,
  * j < n_pos.  Errors: SV_ERR_NULL; SV_ERR_SHAPE if a size is negative.

@@ -16,7 +16,9 @@ notes):
 * A position j of request r is verified when every earlier position was
   accepted and j < b_r: positions 0 .. min(L_r, b_r - 1).  Positions below L_r
   were accepted, position L_r (when L_r < b_r) was rejected, later positions
-  are unobserved.  Requests with L_r = -1 (a fault) contribute nothing.
+  are unobserved.  Requests whose outcome is not a verify result (L_r = -1
+  after a fault, or L_r, b_r outside 0 <= L_r <= b_r <= k_max) contribute
+  nothing.
 * The model estimates the conditional acceptance of position j — the
   quantity the budget multiplies into survivals — as
   c_j = sigmoid(alpha_j + beta * x), x = log2 q(d_j) clamped to [-64, 0], the
@@ -40,18 +42,19 @@ def feature(q):
     return min(0.0, max(X_MIN, math.log2(q)))
 
 
-def verified_positions(accepted, cu_rows):
-    """Per request: (b_r, L_r, list of (j, y)) of the verified positions."""
+def verified_positions(accepted, cu_rows, k_max):
+    """Per request: (counted, list of (j, y)) of the verified positions."""
     n = len(accepted)
     out = []
     for r in range(n):
         b = int(cu_rows[r + 1]) - int(cu_rows[r]) - 1
         L = int(accepted[r])
+        counted = 0 <= L <= b <= k_max
         obs = []
-        if L >= 0 and b >= 0:
+        if counted:
             for j in range(min(L, b - 1) + 1 if b > 0 else 0):
                 obs.append((j, 1 if j < L else 0))
-        out.append((b, L, obs))
+        out.append((counted, L, obs))
     return out
 
 
@@ -67,8 +70,8 @@ def accept_stats(accepted, cu_rows, k_max):
     attempted = np.zeros(k_max, dtype=np.int64)
     accepted_at = np.zeros(k_max, dtype=np.int64)
     requests = emitted = 0
-    for b, L, obs in verified_positions(accepted, cu_rows):
-        if L < 0:
+    for counted, L, obs in verified_positions(accepted, cu_rows, k_max):
+        if not counted:
             continue
         requests += 1
         emitted += L + 1
@@ -100,7 +103,7 @@ def gradient(theta, q_draft, accepted, cu_rows, k_max):
     q = np.asarray(q_draft, dtype=np.float64).reshape(-1, k_max)
     g = np.zeros(k_max + 1, dtype=np.float64)
     count = 0
-    for r, (b, L, obs) in enumerate(verified_positions(accepted, cu_rows)):
+    for r, (_c, _L, obs) in enumerate(verified_positions(accepted, cu_rows, k_max)):
         for j, y in obs:
             x = feature(q[r, j])
             err = sigmoid(float(theta[j]) + float(theta[k_max]) * x) - y
@@ -114,7 +117,7 @@ def log_loss(theta, q_draft, accepted, cu_rows, k_max):
     """Sum over verified positions of -log P(outcome) (used by the pins)."""
     q = np.asarray(q_draft, dtype=np.float64).reshape(-1, k_max)
     total = 0.0
-    for r, (b, L, obs) in enumerate(verified_positions(accepted, cu_rows)):
+    for r, (_c, _L, obs) in enumerate(verified_positions(accepted, cu_rows, k_max)):
         for j, y in obs:
             z = float(theta[j]) + float(theta[k_max]) * feature(q[r, j])
             # -log sigmoid(z) = log(1 + e^-z); -log(1 - sigmoid(z)) = log(1 + e^z)

@@ -195,6 +195,23 @@ def test_verify_stages_validation():
         assert sv._lib.sv_verify_stages(*base.values(), ok, None) == sv.SV_ERR_WORKSPACE
 
 
+def test_calibration_host_validation():
+    lib = sv._lib
+    assert lib.sv_accept_stats(FAKE, FAKE, -1, 3, FAKE, FAKE, FAKE, None) == sv.SV_ERR_SHAPE
+    assert lib.sv_accept_stats(FAKE, FAKE, 4, 65, FAKE, FAKE, FAKE, None) == sv.SV_ERR_SHAPE
+    assert lib.sv_accept_stats(FAKE, FAKE, 4, 3, FAKE, FAKE, None, None) == sv.SV_ERR_NULL
+    assert lib.sv_accept_stats(None, FAKE, 4, 3, FAKE, FAKE, FAKE, None) == sv.SV_ERR_NULL
+    assert lib.sv_calibrate_update(FAKE, FAKE, FAKE, FAKE, 4, 65, 0.1, None, None) == sv.SV_ERR_SHAPE
+    assert lib.sv_calibrate_update(FAKE, FAKE, FAKE, FAKE, 4, 3, -0.1, None, None) == sv.SV_ERR_VALUE
+    assert lib.sv_calibrate_update(FAKE, FAKE, FAKE, FAKE, 4, 3, float("nan"), None,
+                                   None) == sv.SV_ERR_VALUE
+    assert lib.sv_calibrate_update(None, FAKE, FAKE, FAKE, 4, 3, 0.1, None, None) == sv.SV_ERR_NULL
+    assert lib.sv_calibrate_update(FAKE, None, FAKE, FAKE, 4, 3, 0.1, None, None) == sv.SV_ERR_NULL
+    assert lib.sv_calibrate_predict(FAKE, FAKE, 4, 65, FAKE, None) == sv.SV_ERR_SHAPE
+    assert lib.sv_calibrate_predict(FAKE, None, 4, 3, FAKE, None) == sv.SV_ERR_NULL
+    assert lib.sv_calibrate_predict(None, None, 0, 3, None, None) == sv.SV_OK
+
+
 def test_philox_host_validation():
     assert sv._lib.sv_philox_uniforms(0, 0, -1, 3, FAKE, FAKE, None) == sv.SV_ERR_SHAPE
     assert sv._lib.sv_philox_uniforms(0, 0, 2, 3, None, FAKE, None) == sv.SV_ERR_NULL

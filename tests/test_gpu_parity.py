@@ -453,3 +453,95 @@ def test_verify_reuses_an_uncleared_workspace():
         for key in want:
             np.testing.assert_array_equal(got[key].cpu().numpy(), want[key].cpu().numpy(),
                                           err_msg=f"call {i}: {key}")
+
+
+# ----------------------------------------- acceptance statistics, calibration
+
+def random_outcomes(rng, n, k):
+    kept = rng.integers(0, k + 1, n)
+    cu = np.concatenate([[0], np.cumsum(kept + 1)]).astype(np.int32)
+    L = np.array([rng.integers(0, b + 1) for b in kept], dtype=np.int32)
+    L[rng.uniform(size=n) < 0.05] = -1          # faulted requests
+    q = np.where(rng.uniform(size=(n, k)) < 0.05, 0.0,
+                 rng.uniform(1e-4, 1.0, (n, k))).astype(np.float32)
+    q[rng.uniform(size=(n, k)) < 0.01] = np.nan
+    return L, cu, q
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (256, 7), (3000, 15), (100, 64), (5, 0)])
+def test_accept_stats(n, k):
+    import adaptive_draft_verification_amd as sv
+    rng = np.random.default_rng(n * 7 + k)
+    L, cu, _ = random_outcomes(rng, n, k)
+    if n > 2:
+        L[1] = (cu[2] - cu[1] - 1) + 1  # more accepted than kept: not a verify result
+    att = torch.zeros(k, dtype=torch.int64, device="cuda")
+    acc = torch.zeros(k, dtype=torch.int64, device="cuda")
+    tot = torch.zeros(2, dtype=torch.int64, device="cuda")
+    for _ in range(2):  # counters accumulate
+        sv.sv_accept_stats(to_dev(L), to_dev(cu), att, acc, tot)
+    torch.cuda.synchronize()
+    o = oracle.accept_stats(L, cu, k)
+    np.testing.assert_array_equal(att.cpu().numpy(), 2 * o["attempted"])
+    np.testing.assert_array_equal(acc.cpu().numpy(), 2 * o["accepted_at"])
+    assert tot.cpu().numpy().tolist() == [2 * o["requests"], 2 * o["emitted"]]
+
+
+@pytest.mark.parametrize("n,k,seed", [(1, 1, 0), (64, 7, 1), (2500, 7, 2), (300, 64, 3),
+                                      (50, 3, 4)])
+def test_calibrate_update_and_predict(n, k, seed):
+    """fp32 on the device against the oracle's fp64: theta relative 1e-5
+    (sums of a few thousand sigmoid errors in fp32), the count exact."""
+    import adaptive_draft_verification_amd as sv
+    rng = np.random.default_rng(seed)
+    L, cu, q = random_outcomes(rng, n, k)
+    theta = rng.normal(0, 1, k + 1).astype(np.float32)
+    th = to_dev(theta)
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sv.sv_calibrate_update(th, to_dev(q), to_dev(L), to_dev(cu), 0.5, cnt)
+    torch.cuda.synchronize()
+    want, count = oracle.calibrate_update(theta.astype(np.float64), q, L, cu, k, 0.5)
+    assert int(cnt.cpu()[0]) == count
+    np.testing.assert_allclose(th.cpu().numpy(), want, rtol=1e-5, atol=1e-6)
+    conf = torch.empty(n, k, dtype=torch.float32, device="cuda")
+    sv.sv_calibrate_predict(th, to_dev(q), conf)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(conf.cpu().numpy(),
+                               oracle.calibrate_predict(th.cpu().numpy().astype(np.float64), q, k),
+                               rtol=2e-6, atol=1e-7)
+
+
+def test_calibration_from_a_verify_step():
+    """budget -> pack -> verify on the device, then the step's statistics and one
+    calibration step from the verify outputs, each against the oracle fed the
+    same outputs."""
+    import adaptive_draft_verification_amd as sv
+    w = workloads.make("b64_v128256")
+    cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+    o_b = oracle.budget_select(w.conf, w.draft_len, w.k_max, cost, w.t_base, w.n_bonus)
+    toks = w.draft_tokens("stochastic")
+    o_p = oracle.pack_varlen(o_b["kept"], w.last_token, toks, w.k_max)
+    target = workloads.assemble_target(w, o_p["cu_rows"], o_b["kept"])
+    draft = workloads.assemble_draft(w, o_b["kept"])
+    dt = logits_dtype(w)
+    b = sv.budget_select(to_dev(w.conf), to_dev(w.draft_len), to_dev(cost), w.t_base, w.n_bonus)
+    p = sv.pack_varlen(b["kept"], to_dev(w.last_token), to_dev(toks))
+    v = sv.verify(to_dev(target, dt), to_dev(draft, dt), to_dev(toks), p["cu_rows"],
+                  sv.SV_STOCHASTIC, w.tau, w.seed, w.step)
+    k = w.k_max
+    att = torch.zeros(k, dtype=torch.int64, device="cuda")
+    acc = torch.zeros(k, dtype=torch.int64, device="cuda")
+    tot = torch.zeros(2, dtype=torch.int64, device="cuda")
+    sv.sv_accept_stats(v["accepted"], p["cu_rows"], att, acc, tot)
+    theta = torch.zeros(k + 1, dtype=torch.float32, device="cuda")
+    sv.sv_calibrate_update(theta, v["q_draft"], v["accepted"], p["cu_rows"], 1.0)
+    torch.cuda.synchronize()
+    L = v["accepted"].cpu().numpy()
+    cu = p["cu_rows"].cpu().numpy()
+    q = v["q_draft"].cpu().numpy()
+    o = oracle.accept_stats(L, cu, k)
+    np.testing.assert_array_equal(att.cpu().numpy(), o["attempted"])
+    np.testing.assert_array_equal(acc.cpu().numpy(), o["accepted_at"])
+    assert tot.cpu().numpy().tolist() == [o["requests"], o["emitted"]] and o["requests"] == w.n
+    want, _ = oracle.calibrate_update(np.zeros(k + 1), q, L, cu, k, 1.0)
+    np.testing.assert_allclose(theta.cpu().numpy(), want, rtol=1e-5, atol=1e-6)

@@ -27,6 +27,9 @@ def test_hand_case():
     assert res["attempted"].tolist() == [2, 2, 0, 0]
     assert res["accepted_at"].tolist() == [2, 1, 0, 0]
     assert res["requests"] == 3 and res["emitted"] == 2 + 3 + 1
+    # an accepted count above the kept count is not a verify result: skipped
+    res = cal.accept_stats([1, 3, 0], cu_from_kept([3, 2, 0]), 4)
+    assert res["attempted"].tolist() == [1, 1, 0, 0] and res["requests"] == 2
 
 
 def test_fos_per_position_table():
