@@ -324,9 +324,14 @@ def main():
     if args.full_k_iters > 0:
         cu_full = torch.empty(n + 1, dtype=torch.int32, device=dev)
         sv.sv_pack_varlen(dl_d, last_d, toks_d, cu_full, row_req, row_pos, packed, err)
-        full_reps = [(tgt_full_d, drf_full_d)]
+        # every draft kept: request r's rows 0..K_r packed at cu_full[r] (the layout a
+        # varlen target forward writes), gathered from the per-request stride K+1
+        full_idx = np.concatenate([r * (K + 1) + np.arange(int(w.draft_len[r]) + 1)
+                                   for r in range(n)])
+        tgt_packed = tgt_full_d.index_select(0, d(full_idx.astype(np.int64)))
+        full_reps = [(tgt_packed, drf_full_d)]
         if args.replicas > 1:
-            full_reps.append((tgt_full_d.clone(), replicas[1][1]))
+            full_reps.append((tgt_packed.clone(), replicas[1][1]))
         rows_tf = int(cu_full[-1].item())
         rows_df = int(w.draft_len.sum())
         kw = dict(reps=full_reps, cu_rows=cu_full, kept_in=True)
