@@ -37,9 +37,15 @@ Parity pin status (what the oracle is checked against, in tests/):
 * accept_stats — pinned by a hand-derived case and by the FOS per-position
   table (conditional column = accepted / verified, cumulative = running
   product, mean acceptance length = 1 + sum of the cumulative column).
+* draft_features (entropy in bits and largest probability of a draft row) —
+  pinned by closed forms on uniform, k-point and two-point rows, by scipy's
+  entropy and softmax on random rows, and by invariants (logit shift,
+  temperature folded into the logits, min-entropy and support bounds,
+  entropy rising with temperature).
 * calibrate_update / calibrate_predict — pinned by finite differences of an
   independently written log-loss, by the gradient vanishing (in mean) at the
-  parameters that generated the outcomes, and by the sign of an update.
+  parameters that generated the outcomes, by absent features reading as 0,
+  and by the sign of an update.
 * cost_table_prepare — pinned by the 121 -> 128 padding example on the
   agentlens page and by monotonicity.
 * pack_varlen — pinned by hand-derived golden fixtures and capacity formula.
@@ -66,6 +72,7 @@ from .budget import (
 )
 from .uniform_k import uniform_k_select
 from .calibrate import accept_stats, calibrate_update, predict as calibrate_predict
+from .features import draft_features
 from .pack import pack_varlen, DEV_BAD_KEPT
 from .verify import (
     row_probs,
@@ -86,7 +93,7 @@ __all__ = [
     "philox4x32_10", "uniforms", "PHILOX_ROUNDS",
     "clamp_confidence", "survival", "cost_table_prepare", "rank_slots",
     "fixed_point", "expected_tokens", "budget_score", "budget_select", "uniform_k_select",
-    "accept_stats", "calibrate_update", "calibrate_predict",
+    "accept_stats", "calibrate_update", "calibrate_predict", "draft_features",
     "pack_varlen", "row_probs", "accept", "residual_weights", "inverse_cdf",
     "row_is_faulty", "verify_request", "verify", "GREEDY", "STOCHASTIC",
     "DEV_BAD_DRAFT_LEN", "DEV_BAD_COST", "DEV_BAD_KEPT", "DEV_BAD_CU_ROWS",

@@ -34,6 +34,7 @@ row offsets, draft ids outside [0, V), and rows holding NaN or +inf or only
 
 import numpy as np
 
+from .features import draft_features
 from .philox import uniforms
 
 STOCHASTIC = 0
@@ -102,9 +103,10 @@ def verify_request(r, trows, drows, dtoks, b, vocab, mode, tau, seed, step,
     (drafts < forced_l accepted, forced_l rejected if < b); the result then
     lists every forced decision that disagrees with the natural one.
 
-    Returns a dict with tokens, L, p_d, q_d, u, ratio, residual_mass, fault.
+    Returns a dict with tokens, L, p_d, q_d, u, ratio, q_entropy, q_max
+    (the draft-row features of positions 0..b-1), residual_mass, fault.
     """
-    out = dict(tokens=[], L=-1, p_d=[], q_d=[], u=[], ratio=[],
+    out = dict(tokens=[], L=-1, p_d=[], q_d=[], u=[], ratio=[], q_entropy=[], q_max=[],
                residual_mass=-1.0, fault=0, overridden=[], weights=None, v=None)
     for j in range(b):
         if not (0 <= int(dtoks[j]) < vocab):
@@ -131,6 +133,10 @@ def verify_request(r, trows, drows, dtoks, b, vocab, mode, tau, seed, step,
 
     p = [row_probs(trows[j], tau) for j in range(b + 1)]
     q = [row_probs(drows[j], tau) for j in range(b)]
+    for j in range(b):
+        h, m = draft_features(drows[j], tau)
+        out["q_entropy"].append(h)
+        out["q_max"].append(m)
     decisions = []
     for j in range(b):
         d = int(dtoks[j])
@@ -175,7 +181,8 @@ def verify(target, draft, draft_tokens, cu_rows, k_max, vocab, mode, temperature
     cu_rows[r+1]-1).  draft: [n*k_max, V] (or [n, k_max, V]) draft logits,
     row r*k_max + j for position j; None in greedy mode.  forced: optional
     {r: L} replays.  Returns dict(tokens [n, k_max+1], accepted [n], p_draft,
-    q_draft [n, k_max], residual_mass [n], dev_error, per_request).
+    q_draft, q_entropy, q_max [n, k_max] (stochastic, kept positions; -1
+    elsewhere), residual_mass [n], dev_error, per_request).
     """
     cu_rows = np.asarray(cu_rows, dtype=np.int64)
     n = len(cu_rows) - 1
@@ -189,6 +196,8 @@ def verify(target, draft, draft_tokens, cu_rows, k_max, vocab, mode, temperature
     accepted = np.full(n, -1, dtype=np.int32)
     p_draft = np.full((n, k_max), -1.0)
     q_draft = np.full((n, k_max), -1.0)
+    q_entropy = np.full((n, k_max), -1.0)
+    q_max = np.full((n, k_max), -1.0)
     resid = np.full(n, -1.0)
     err = 0
     per_request = []
@@ -215,6 +224,8 @@ def verify(target, draft, draft_tokens, cu_rows, k_max, vocab, mode, temperature
         if mode == STOCHASTIC:
             p_draft[r, :b] = res["p_d"]
             q_draft[r, :b] = res["q_d"]
+            q_entropy[r, :b] = res["q_entropy"]
+            q_max[r, :b] = res["q_max"]
             resid[r] = res["residual_mass"]
     return dict(tokens=tokens, accepted=accepted, p_draft=p_draft, q_draft=q_draft,
-                residual_mass=resid, dev_error=err, per_request=per_request)
+                q_entropy=q_entropy, q_max=q_max, residual_mass=resid, dev_error=err, per_request=per_request)

@@ -57,35 +57,38 @@ def test_fos_per_position_table():
 
 
 def synthetic(rng, n, k, theta):
-    """Draft probabilities and outcomes drawn from the logistic model theta:
-    a request stops at its first rejection (the verify rule)."""
+    """Draft features and outcomes drawn from the logistic model theta: a
+    request stops at its first rejection (the verify rule)."""
     kept = rng.integers(0, k + 1, n)
     q = np.where(rng.uniform(size=(n, k)) < 0.05, 0.0, rng.uniform(0.01, 1.0, (n, k)))
+    h = rng.uniform(0.0, 8.0, (n, k))
+    m = rng.uniform(0.05, 1.0, (n, k))
     L = np.zeros(n, dtype=np.int64)
     for r in range(n):
         j = 0
         while j < kept[r]:
-            p = cal.sigmoid(theta[j] + theta[k] * cal.feature(q[r, j]))
-            if rng.uniform() >= p:
+            z = (theta[j] + theta[k] * cal.feature(q[r, j]) + theta[k + 1] * h[r, j]
+                 + theta[k + 2] * m[r, j])
+            if rng.uniform() >= cal.sigmoid(z):
                 break
             j += 1
         L[r] = j
-    return q, L, cu_from_kept(kept)
+    return q, h, m, L, cu_from_kept(kept)
 
 
 def test_gradient_matches_finite_differences():
     rng = np.random.default_rng(3)
     k = 4
-    theta = rng.normal(0, 1, k + 1)
-    q, L, cu = synthetic(rng, 300, k, rng.normal(0, 1, k + 1))
-    g, count = cal.gradient(theta, q, L, cu, k)
+    theta = rng.normal(0, 0.3, k + 3)
+    q, h, m, L, cu = synthetic(rng, 300, k, rng.normal(0, 0.3, k + 3))
+    g, count = cal.gradient(theta, q, L, cu, k, h, m)
     assert count > 0
-    h = 1e-6
-    for i in range(k + 1):
+    eps = 1e-6
+    for i in range(k + 3):
         tp, tm = theta.copy(), theta.copy()
-        tp[i] += h
-        tm[i] -= h
-        fd = (cal.log_loss(tp, q, L, cu, k) - cal.log_loss(tm, q, L, cu, k)) / (2 * h)
+        tp[i] += eps
+        tm[i] -= eps
+        fd = (cal.log_loss(tp, q, L, cu, k, h, m) - cal.log_loss(tm, q, L, cu, k, h, m)) / (2 * eps)
         assert g[i] == pytest.approx(fd, rel=1e-5, abs=1e-6), i
 
 
@@ -94,28 +97,50 @@ def test_gradient_is_unbiased_at_the_generating_parameters():
     clearly not ~0 at a shifted theta."""
     rng = np.random.default_rng(5)
     k = 3
-    star = np.array([1.2, 0.4, -0.3, 0.25])
-    q, L, cu = synthetic(rng, 40000, k, star)
-    g, count = cal.gradient(star, q, L, cu, k)
-    assert np.all(np.abs(g / count) < 0.01), g / count
-    off = star + np.array([0.5, -0.5, 0.5, 0.1])
-    g2, _ = cal.gradient(off, q, L, cu, k)
+    star = np.array([1.2, 0.4, -0.3, 0.25, -0.2, 0.8])
+    q, h, m, L, cu = synthetic(rng, 40000, k, star)
+    g, count = cal.gradient(star, q, L, cu, k, h, m)
+    assert np.all(np.abs(g / count) < 0.012), g / count
+    off = star + np.array([0.5, -0.5, 0.5, 0.1, 0.1, -0.3])
+    g2, _ = cal.gradient(off, q, L, cu, k, h, m)
     assert np.max(np.abs(g2 / count)) > 0.03
+
+
+def test_absent_features_read_as_zero():
+    rng = np.random.default_rng(8)
+    k = 3
+    theta = rng.normal(0, 0.5, k + 3)
+    q, h, m, L, cu = synthetic(rng, 200, k, theta)
+    g0, c0 = cal.gradient(theta, q, L, cu, k)
+    g1, c1 = cal.gradient(theta, q, L, cu, k, np.zeros_like(h), np.zeros_like(m))
+    np.testing.assert_array_equal(g0, g1)
+    assert c0 == c1 and g0[k + 1] == 0 and g0[k + 2] == 0
 
 
 def test_update_moves_toward_the_outcomes():
     k = 2
-    theta = np.zeros(k + 1)
+    theta = np.zeros(k + 3)
     q = np.full((4, k), 0.5)
     all_acc, _ = cal.calibrate_update(theta, q, [2, 2, 2, 2], cu_from_kept([2] * 4), k, 1.0)
     all_rej, _ = cal.calibrate_update(theta, q, [0, 0, 0, 0], cu_from_kept([2] * 4), k, 1.0)
     assert all_acc[0] > 0 and all_acc[1] > 0
     assert all_rej[0] < 0 and all_rej[1] == 0  # position 1 never verified
+    # x_1 = log2 0.5 = -1 < 0: accepting pushes beta_1 down, rejecting up
+    assert all_acc[k] < 0 and all_rej[k] > 0
 
 
-def test_predict_and_feature():
+def test_predict_and_features():
     assert cal.feature(0.0) == -64 and cal.feature(1.0) == 0 and cal.feature(0.25) == -2
     assert cal.feature(float("nan")) == -64 and cal.feature(2.0) == 0
-    c = cal.predict(np.array([0.0, math.log(3.0), 1.0]), np.array([[1.0, 0.5]]), 2)
+    assert cal.entropy_feature(-1.0) == 0 and cal.entropy_feature(float("nan")) == 0
+    assert cal.entropy_feature(3.5) == 3.5 and cal.entropy_feature(100.0) == 64
+    assert cal.max_feature(-1.0) == 0 and cal.max_feature(float("nan")) == 0
+    assert cal.max_feature(0.25) == 0.25 and cal.max_feature(1.5) == 1
+    theta = np.array([0.0, math.log(3.0), 1.0, 0.5, -2.0])
+    c = cal.predict(theta, np.array([[1.0, 0.5]]), 2)
     assert c[0, 0] == pytest.approx(0.5)
     assert c[0, 1] == pytest.approx(cal.sigmoid(math.log(3.0) - 1.0))
+    c = cal.predict(theta, np.array([[1.0, 0.5]]), 2, np.array([[2.0, 4.0]]),
+                    np.array([[0.5, 0.25]]))
+    assert c[0, 0] == pytest.approx(cal.sigmoid(0.5 * 2.0 - 2.0 * 0.5))
+    assert c[0, 1] == pytest.approx(cal.sigmoid(math.log(3.0) - 1.0 + 0.5 * 4.0 - 2.0 * 0.25))
