@@ -58,14 +58,14 @@ def _load():
                                                vp, vp]),
         "sv_pack_varlen": (ctypes.c_int, [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]),
         "sv_verify": (ctypes.c_int, [vp, i64, i64, vp, i64, ctypes.c_int, i32, vp, vp, i32, i32,
-                                     ctypes.c_int, f32, u64, u64, vp, vp, vp, vp, vp, vp, vp, sz,
-                                     vp]),
+                                     ctypes.c_int, f32, u64, u64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, sz, vp]),
         "sv_verify_stages": (ctypes.c_int, [vp, i64, i64, vp, i64, ctypes.c_int, i32, vp, vp, i32,
                                             i32, ctypes.c_int, f32, u64, u64, vp, vp, vp, vp, vp,
-                                            vp, vp, sz, i32, vp]),
+                                            vp, vp, vp, vp, sz, i32, vp]),
         "sv_accept_stats": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp, vp]),
-        "sv_calibrate_update": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, f32, vp, vp]),
-        "sv_calibrate_predict": (ctypes.c_int, [vp, vp, i32, i32, vp, vp]),
+        "sv_calibrate_update": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp]),
+        "sv_calibrate_predict": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, vp, vp]),
         "sv_philox_uniforms": (ctypes.c_int, [u64, u64, i32, i32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -200,7 +200,7 @@ _DTYPES = {torch.bfloat16: SV_BF16, torch.float32: SV_F32}
 
 def _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
                  out_tokens, out_accepted, ws, out_p_draft, out_q_draft, out_residual_mass,
-                 dev_error, vocab):
+                 dev_error, vocab, out_q_entropy, out_q_max):
     if target.dtype not in _DTYPES:
         raise ValueError("logits must be bfloat16 or float32")
     _dev(target, target.dtype, "target", 2)
@@ -211,7 +211,8 @@ def _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, 
     _dev(out_tokens, torch.int32, "out_tokens", 2)
     _dev(out_accepted, torch.int32, "out_accepted", 1)
     _dev(ws, torch.uint8, "ws", 1)
-    for name, t in (("out_p_draft", out_p_draft), ("out_q_draft", out_q_draft)):
+    for name, t in (("out_p_draft", out_p_draft), ("out_q_draft", out_q_draft),
+                    ("out_q_entropy", out_q_entropy), ("out_q_max", out_q_max)):
         _dev(t, torch.float32, name, 2)
     _dev(out_residual_mass, torch.float32, "out_residual_mass", 1)
     _dev(dev_error, torch.int32, "dev_error", 1)
@@ -222,37 +223,41 @@ def _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, 
         raise ValueError("cu_rows [n+1], out_tokens [n, k_max+1], out_accepted [n]")
     if draft is not None and draft.shape[0] < n * k_max:
         raise ValueError("draft must hold n*k_max rows")
-    for t in (out_p_draft, out_q_draft):
+    for t in (out_p_draft, out_q_draft, out_q_entropy, out_q_max):
         if t is not None and tuple(t.shape) != (n, k_max):
-            raise ValueError("out_p_draft/out_q_draft must be [n, k_max]")
+            raise ValueError("out_p_draft, out_q_draft, out_q_entropy, out_q_max must be "
+                             "[n, k_max]")
     if out_residual_mass is not None and out_residual_mass.numel() != n:
         raise ValueError("out_residual_mass must have n entries")
     return [_ptr(target), target.shape[1], target.shape[0], _ptr(draft),
             0 if draft is None else draft.shape[1], _DTYPES[target.dtype], V,
             _ptr(draft_tokens), _ptr(cu_rows), n, k_max, int(mode), float(temperature),
             int(seed), int(step), _ptr(out_tokens), _ptr(out_accepted), _ptr(out_p_draft),
-            _ptr(out_q_draft), _ptr(out_residual_mass), _ptr(dev_error), _ptr(ws), ws.numel()]
+            _ptr(out_q_draft), _ptr(out_residual_mass), _ptr(out_q_entropy), _ptr(out_q_max),
+            _ptr(dev_error), _ptr(ws), ws.numel()]
 
 
 def sv_verify(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step, out_tokens,
               out_accepted, ws, out_p_draft=None, out_q_draft=None, out_residual_mass=None,
-              dev_error=None, vocab=None, stream=None):
+              dev_error=None, vocab=None, stream=None, out_q_entropy=None, out_q_max=None):
     """target [rows, >=V] and draft [n*k_max, >=V] (bf16 or f32, row stride = shape[1]);
     draft_tokens [n, k_max] i32; cu_rows [n+1] i32; ws: uint8 device buffer of
-    sv_verify_workspace_bytes(n, k_max) bytes."""
+    sv_verify_workspace_bytes(n, k_max) bytes; out_q_entropy / out_q_max [n, k_max] f32
+    ask pass 1 for the draft-row features."""
     args = _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
                         out_tokens, out_accepted, ws, out_p_draft, out_q_draft,
-                        out_residual_mass, dev_error, vocab)
+                        out_residual_mass, dev_error, vocab, out_q_entropy, out_q_max)
     _check(_lib.sv_verify(*args, _stream(stream)), "sv_verify")
 
 
 def sv_verify_stages(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
                      out_tokens, out_accepted, ws, stages, out_p_draft=None, out_q_draft=None,
-                     out_residual_mass=None, dev_error=None, vocab=None, stream=None):
+                     out_residual_mass=None, dev_error=None, vocab=None, stream=None,
+                     out_q_entropy=None, out_q_max=None):
     """sv_verify restricted to pass 1 (stages=1), pass 2 (stages=2) or both (3)."""
     args = _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
                         out_tokens, out_accepted, ws, out_p_draft, out_q_draft,
-                        out_residual_mass, dev_error, vocab)
+                        out_residual_mass, dev_error, vocab, out_q_entropy, out_q_max)
     _check(_lib.sv_verify_stages(*args, int(stages), _stream(stream)), "sv_verify_stages")
 
 
@@ -272,31 +277,41 @@ def sv_accept_stats(accepted, cu_rows, attempted, accepted_at, totals, stream=No
            "sv_accept_stats")
 
 
-def sv_calibrate_update(theta, q_draft, accepted, cu_rows, lr, count_out=None, stream=None):
-    """theta [k_max+1] f32 (in place), q_draft [n, k_max] f32, accepted [n], cu_rows [n+1]."""
-    _dev(theta, torch.float32, "theta", 1)
+def _features(q_draft, q_entropy, q_max):
     _dev(q_draft, torch.float32, "q_draft", 2)
+    for name, t in (("q_entropy", q_entropy), ("q_max", q_max)):
+        _dev(t, torch.float32, name, 2)
+        if t is not None and t.shape != q_draft.shape:
+            raise ValueError(f"{name} must have q_draft's shape")
+    return q_draft.shape
+
+
+def sv_calibrate_update(theta, q_draft, accepted, cu_rows, lr, count_out=None, stream=None,
+                        q_entropy=None, q_max=None):
+    """theta [k_max+3] f32 (in place); q_draft, q_entropy, q_max [n, k_max] f32 (the last
+    two may be None: feature 0); accepted [n]; cu_rows [n+1]."""
+    _dev(theta, torch.float32, "theta", 1)
     _dev(accepted, torch.int32, "accepted", 1)
     _dev(cu_rows, torch.int32, "cu_rows", 1)
     _dev(count_out, torch.int32, "count_out", 1)
-    n, k_max = q_draft.shape
-    if theta.numel() != k_max + 1 or accepted.numel() != n or cu_rows.numel() != n + 1:
-        raise ValueError("theta [k_max+1], accepted [n], cu_rows [n+1]")
-    _check(_lib.sv_calibrate_update(_ptr(theta), _ptr(q_draft), _ptr(accepted), _ptr(cu_rows), n,
-                                    k_max, float(lr), _ptr(count_out), _stream(stream)),
+    n, k_max = _features(q_draft, q_entropy, q_max)
+    if theta.numel() != k_max + 3 or accepted.numel() != n or cu_rows.numel() != n + 1:
+        raise ValueError("theta [k_max+3], accepted [n], cu_rows [n+1]")
+    _check(_lib.sv_calibrate_update(_ptr(theta), _ptr(q_draft), _ptr(q_entropy), _ptr(q_max),
+                                    _ptr(accepted), _ptr(cu_rows), n, k_max, float(lr),
+                                    _ptr(count_out), _stream(stream)),
            "sv_calibrate_update")
 
 
-def sv_calibrate_predict(theta, q_draft, conf, stream=None):
-    """conf [n, k_max] f32 <- sigmoid(alpha_j + beta * log2 q)."""
+def sv_calibrate_predict(theta, q_draft, conf, stream=None, q_entropy=None, q_max=None):
+    """conf [n, k_max] f32 <- sigmoid(alpha_j + beta . x(q, entropy, max prob))."""
     _dev(theta, torch.float32, "theta", 1)
-    _dev(q_draft, torch.float32, "q_draft", 2)
     _dev(conf, torch.float32, "conf", 2)
-    n, k_max = q_draft.shape
-    if theta.numel() != k_max + 1 or tuple(conf.shape) != (n, k_max):
-        raise ValueError("theta [k_max+1], conf [n, k_max]")
-    _check(_lib.sv_calibrate_predict(_ptr(theta), _ptr(q_draft), n, k_max, _ptr(conf),
-                                     _stream(stream)),
+    n, k_max = _features(q_draft, q_entropy, q_max)
+    if theta.numel() != k_max + 3 or tuple(conf.shape) != (n, k_max):
+        raise ValueError("theta [k_max+3], conf [n, k_max]")
+    _check(_lib.sv_calibrate_predict(_ptr(theta), _ptr(q_draft), _ptr(q_entropy), _ptr(q_max), n,
+                                     k_max, _ptr(conf), _stream(stream)),
            "sv_calibrate_predict")
 
 
@@ -355,9 +370,10 @@ def pack_varlen(kept, last_token, draft_tokens, stream=None):
 
 
 def verify(target, draft, draft_tokens, cu_rows, mode, temperature=1.0, seed=0, step=0,
-           vocab=None, stream=None, stages=None, ws=None):
-    """Allocating wrapper: sv_verify (one launch), or sv_verify_stages(stages) (the
-    two-launch path) when `stages` is given.  ws: a zero-filled workspace to reuse."""
+           vocab=None, stream=None, stages=None, ws=None, features=False):
+    """Allocating wrapper: sv_verify, or sv_verify_stages(stages) when `stages` is given.
+    ws: a workspace to reuse.  features: also return the draft-row features q_entropy and
+    q_max (pass 1 then accumulates them)."""
     dev = target.device
     n, k_max = draft_tokens.shape
     if ws is None:
@@ -369,12 +385,17 @@ def verify(target, draft, draft_tokens, cu_rows, mode, temperature=1.0, seed=0, 
                q_draft=torch.empty(n, k_max, dtype=torch.float32, device=dev),
                residual_mass=torch.empty(n, dtype=torch.float32, device=dev),
                dev_error=torch.zeros(1, dtype=torch.int32, device=dev))
+    if features:
+        out["q_entropy"] = torch.empty(n, k_max, dtype=torch.float32, device=dev)
+        out["q_max"] = torch.empty(n, k_max, dtype=torch.float32, device=dev)
+    feat = dict(out_q_entropy=out.get("q_entropy"), out_q_max=out.get("q_max"))
     if stages is None:
         sv_verify(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
                   out["tokens"], out["accepted"], ws, out["p_draft"], out["q_draft"],
-                  out["residual_mass"], out["dev_error"], vocab, stream)
+                  out["residual_mass"], out["dev_error"], vocab, stream, **feat)
     else:
         sv_verify_stages(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
                          out["tokens"], out["accepted"], ws, stages, out["p_draft"],
-                         out["q_draft"], out["residual_mass"], out["dev_error"], vocab, stream)
+                         out["q_draft"], out["residual_mass"], out["dev_error"], vocab, stream,
+                         **feat)
     return out

@@ -125,8 +125,9 @@ sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t
                            int32_t n_req, int32_t k_max, sv_mode mode, float temperature,
                            uint64_t seed, uint64_t step, int32_t* out_tokens,
                            int32_t* out_accepted, float* out_p_draft, float* out_q_draft,
-                           float* out_residual_mass, int32_t* dev_error, void* ws,
-                           size_t ws_bytes, int32_t stages, void* stream) {
+                           float* out_residual_mass, float* out_q_entropy, float* out_q_max,
+                           int32_t* dev_error, void* ws, size_t ws_bytes, int32_t stages,
+                           void* stream) {
     if (stages < 1 || stages > 3) return SV_ERR_VALUE;
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
     if (mode != SV_STOCHASTIC && mode != SV_GREEDY) return SV_ERR_VALUE;
@@ -151,7 +152,7 @@ sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t
                      dtype,         vocab,        draft_tokens, cu_rows,      n_req,
                      k_max,         mode,         temperature,  seed,         step,
                      out_tokens,    out_accepted, out_p_draft,  out_q_draft,  out_residual_mass,
-                     dev_error,     ws,           stages};
+                     out_q_entropy, out_q_max,    dev_error,    ws,           stages};
     return launched(sv::launch_verify(a, as_stream(stream)));
 }
 
@@ -160,12 +161,14 @@ sv_status sv_verify(const void* target_logits, int64_t target_ld, int64_t target
                     const int32_t* draft_tokens, const int32_t* cu_rows, int32_t n_req,
                     int32_t k_max, sv_mode mode, float temperature, uint64_t seed, uint64_t step,
                     int32_t* out_tokens, int32_t* out_accepted, float* out_p_draft,
-                    float* out_q_draft, float* out_residual_mass, int32_t* dev_error, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    float* out_q_draft, float* out_residual_mass, float* out_q_entropy,
+                    float* out_q_max, int32_t* dev_error, void* ws, size_t ws_bytes,
+                    void* stream) {
     return sv_verify_stages(target_logits, target_ld, target_rows, draft_logits, draft_ld, dtype,
                             vocab, draft_tokens, cu_rows, n_req, k_max, mode, temperature, seed,
                             step, out_tokens, out_accepted, out_p_draft, out_q_draft,
-                            out_residual_mass, dev_error, ws, ws_bytes, 3, stream);
+                            out_residual_mass, out_q_entropy, out_q_max, dev_error, ws, ws_bytes,
+                            3, stream);
 }
 
 sv_status sv_accept_stats(const int32_t* accepted, const int32_t* cu_rows, int32_t n_req,
@@ -179,7 +182,8 @@ sv_status sv_accept_stats(const int32_t* accepted, const int32_t* cu_rows, int32
                                             accepted_at, totals, as_stream(stream)));
 }
 
-sv_status sv_calibrate_update(float* theta, const float* q_draft, const int32_t* accepted,
+sv_status sv_calibrate_update(float* theta, const float* q_draft, const float* q_entropy,
+                              const float* q_max, const int32_t* accepted,
                               const int32_t* cu_rows, int32_t n_req, int32_t k_max, float lr,
                               int32_t* count_out, void* stream) {
     if (n_req < 0 || k_max < 0 || k_max > SV_MAX_DRAFT) return SV_ERR_SHAPE;
@@ -187,17 +191,19 @@ sv_status sv_calibrate_update(float* theta, const float* q_draft, const int32_t*
     if (theta == nullptr) return SV_ERR_NULL;
     if (n_req > 0 && (accepted == nullptr || cu_rows == nullptr)) return SV_ERR_NULL;
     if (n_req > 0 && k_max > 0 && q_draft == nullptr) return SV_ERR_NULL;
-    return launched(sv::launch_calibrate_update(theta, q_draft, accepted, cu_rows, n_req, k_max,
-                                                lr, count_out, as_stream(stream)));
+    return launched(sv::launch_calibrate_update(theta, q_draft, q_entropy, q_max, accepted,
+                                                cu_rows, n_req, k_max, lr, count_out,
+                                                as_stream(stream)));
 }
 
-sv_status sv_calibrate_predict(const float* theta, const float* q_draft, int32_t n_req,
-                               int32_t k_max, float* conf, void* stream) {
+sv_status sv_calibrate_predict(const float* theta, const float* q_draft, const float* q_entropy,
+                               const float* q_max, int32_t n_req, int32_t k_max, float* conf,
+                               void* stream) {
     if (n_req < 0 || k_max < 0 || k_max > SV_MAX_DRAFT) return SV_ERR_SHAPE;
     if ((int64_t)n_req * k_max > 0 && (theta == nullptr || q_draft == nullptr || conf == nullptr))
         return SV_ERR_NULL;
-    return launched(sv::launch_calibrate_predict(theta, q_draft, n_req, k_max, conf,
-                                                 as_stream(stream)));
+    return launched(sv::launch_calibrate_predict(theta, q_draft, q_entropy, q_max, n_req, k_max,
+                                                 conf, as_stream(stream)));
 }
 
 sv_status sv_philox_uniforms(uint64_t seed, uint64_t step, int32_t n_req, int32_t n_pos,

@@ -12,8 +12,12 @@
 // 0 .. min(L_r, b_r - 1): those below L_r were accepted, position L_r (when
 // L_r < b_r) rejected.  Requests whose outcome is not a verify result
 // (L_r < 0 after a fault, or outside 0 <= L_r <= b_r <= k_max) are skipped.
-// The model: c_j = sigmoid(alpha_j + beta * x), x = log2 q(d_j) clamped to
-// [-64, 0] (the draft's own log-probability of its token).
+// The model: c_j = sigmoid(alpha_j + beta_1 x_1 + beta_2 x_2 + beta_3 x_3) over
+// three features of draft row j: x_1 = log2 q(d_j) clamped to [-64, 0] (the
+// draft's own log-probability of its token), x_2 = the row's entropy in bits
+// clamped to [0, 64], x_3 = its largest probability clamped to [0, 1]; a
+// feature array left out (null) reads as 0.  theta = [alpha_0 ..
+// alpha_{k_max-1}, beta_1, beta_2, beta_3].
 #include "sv_device.h"
 #include "sv_launch.h"
 
@@ -31,9 +35,25 @@ __device__ __forceinline__ bool outcome(const int32_t* accepted, const int32_t* 
     return *L >= 0 && *L <= *b && *b <= k_max;
 }
 
-__device__ __forceinline__ float feature(float q) {
-    if (!(q > 0.0f)) return kXMin;  // 0, negative or NaN
-    return fminf(0.0f, fmaxf(kXMin, log2f(q)));
+constexpr int kFeat = 3;
+
+struct Features {
+    const float* q;    // q(d_j), [n, k_max]
+    const float* ent;  // draft-row entropy in bits, [n, k_max] or null
+    const float* pmax; // draft-row largest probability, [n, k_max] or null
+};
+
+__device__ __forceinline__ void features(const Features& f, int64_t i, float* x) {
+    const float q = f.q[i];
+    x[0] = q > 0.0f ? fminf(0.0f, fmaxf(kXMin, log2f(q))) : kXMin;  // 0, negative or NaN: floor
+    const float h = f.ent ? f.ent[i] : 0.0f;
+    x[1] = h > 0.0f ? fminf(64.0f, h) : 0.0f;
+    const float m = f.pmax ? f.pmax[i] : 0.0f;
+    x[2] = m > 0.0f ? fminf(1.0f, m) : 0.0f;
+}
+
+__device__ __forceinline__ float logit(const float* th, int j, int k_max, const float* x) {
+    return th[j] + th[k_max] * x[0] + th[k_max + 1] * x[1] + th[k_max + 2] * x[2];
 }
 
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
@@ -96,18 +116,17 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(
 // theta <- theta - lr * grad / N.  One workgroup; each gradient component is
 // a fixed-order block sum (deterministic).
 __global__ __launch_bounds__(kThreads) void calibrate_update_kernel(
-    float* theta, const float* __restrict__ q_draft, const int32_t* __restrict__ accepted,
+    float* theta, Features f, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ cu_rows, int n_req, int k_max, float lr, int32_t* count_out) {
-    __shared__ float th[SV_MAX_DRAFT + 1];
+    __shared__ float th[SV_MAX_DRAFT + kFeat];
     __shared__ float red[kWaves];
-    __shared__ float grad[SV_MAX_DRAFT + 1];
+    __shared__ float grad[SV_MAX_DRAFT + kFeat];
     __shared__ int cnt_s;
     const int tid = threadIdx.x;
-    if (tid <= k_max) th[tid] = theta[tid];
+    if (tid < k_max + kFeat) th[tid] = theta[tid];
     if (tid == 0) cnt_s = 0;
     __syncthreads();
-    const float beta = th[k_max];
-    float g_beta = 0.0f;
+    float g_beta[kFeat] = {0.0f, 0.0f, 0.0f};
     int my_cnt = 0;
     for (int j = 0; j < k_max; ++j) {
         // this thread's requests, in order, that verified position j
@@ -116,33 +135,36 @@ __global__ __launch_bounds__(kThreads) void calibrate_update_kernel(
             int b, L;
             if (!outcome(accepted, cu_rows, r, k_max, &b, &L)) continue;
             if (j > L || j >= b) continue;
-            const float x = feature(q_draft[(int64_t)r * k_max + j]);
-            const float err = sigmoid(th[j] + beta * x) - (j < L ? 1.0f : 0.0f);
+            float x[kFeat];
+            features(f, (int64_t)r * k_max + j, x);
+            const float err = sigmoid(logit(th, j, k_max, x)) - (j < L ? 1.0f : 0.0f);
             g += err;
-            g_beta += err * x;
+#pragma unroll
+            for (int i = 0; i < kFeat; ++i) g_beta[i] += err * x[i];
             ++my_cnt;
         }
         g = block_sum(g, red);
         if (tid == 0) grad[j] = g;
     }
-    g_beta = block_sum(g_beta, red);
+#pragma unroll
+    for (int i = 0; i < kFeat; ++i) {
+        const float g = block_sum(g_beta[i], red);
+        if (tid == 0) grad[k_max + i] = g;
+    }
     if (my_cnt) atomicAdd(&cnt_s, my_cnt);
     __syncthreads();
     const int count = cnt_s;
-    if (tid <= k_max && count > 0) {
-        const float g = tid < k_max ? grad[tid] : g_beta;
-        theta[tid] = th[tid] - lr * (g / (float)count);
-    }
+    if (tid < k_max + kFeat && count > 0) theta[tid] = th[tid] - lr * (grad[tid] / (float)count);
     if (tid == 0 && count_out != nullptr) count_out[0] = count;
 }
 
-__global__ void calibrate_predict_kernel(const float* __restrict__ theta,
-                                         const float* __restrict__ q_draft, int n_req, int k_max,
-                                         float* __restrict__ conf) {
+__global__ void calibrate_predict_kernel(const float* __restrict__ theta, Features f, int n_req,
+                                         int k_max, float* __restrict__ conf) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)n_req * k_max) return;
-    const int j = (int)(i % k_max);
-    conf[i] = sigmoid(theta[j] + theta[k_max] * feature(q_draft[i]));
+    float x[kFeat];
+    features(f, i, x);
+    conf[i] = sigmoid(logit(theta, (int)(i % k_max), k_max, x));
 }
 
 }  // namespace
@@ -157,21 +179,25 @@ hipError_t launch_accept_stats(const int32_t* accepted, const int32_t* cu_rows, 
     return hipGetLastError();
 }
 
-hipError_t launch_calibrate_update(float* theta, const float* q_draft, const int32_t* accepted,
+hipError_t launch_calibrate_update(float* theta, const float* q_draft, const float* q_entropy,
+                                   const float* q_max, const int32_t* accepted,
                                    const int32_t* cu_rows, int n_req, int k_max, float lr,
                                    int32_t* count_out, hipStream_t stream) {
-    hipLaunchKernelGGL(calibrate_update_kernel, dim3(1), dim3(kThreads), 0, stream, theta,
-                       q_draft, accepted, cu_rows, n_req, k_max, lr, count_out);
+    const Features f{q_draft, q_entropy, q_max};
+    hipLaunchKernelGGL(calibrate_update_kernel, dim3(1), dim3(kThreads), 0, stream, theta, f,
+                       accepted, cu_rows, n_req, k_max, lr, count_out);
     return hipGetLastError();
 }
 
-hipError_t launch_calibrate_predict(const float* theta, const float* q_draft, int n_req,
+hipError_t launch_calibrate_predict(const float* theta, const float* q_draft,
+                                    const float* q_entropy, const float* q_max, int n_req,
                                     int k_max, float* conf, hipStream_t stream) {
     const int64_t n = (int64_t)n_req * k_max;
     if (n == 0) return hipSuccess;
     const int threads = 256;
+    const Features f{q_draft, q_entropy, q_max};
     hipLaunchKernelGGL(calibrate_predict_kernel, dim3((unsigned)((n + threads - 1) / threads)),
-                       dim3(threads), 0, stream, theta, q_draft, n_req, k_max, conf);
+                       dim3(threads), 0, stream, theta, f, n_req, k_max, conf);
     return hipGetLastError();
 }
 

@@ -47,6 +47,8 @@ struct VerifyArgs {
     float* out_p_draft;
     float* out_q_draft;
     float* out_residual_mass;
+    float* out_q_entropy;
+    float* out_q_max;
     int32_t* dev_error;
     void* ws;
     int stages;  // bit 0: pass 1 (row statistics), bit 1: pass 2 (decide and draw)
@@ -58,10 +60,12 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_accept_stats(const int32_t* accepted, const int32_t* cu_rows, int n_req,
                                int k_max, uint64_t* attempted, uint64_t* accepted_at,
                                uint64_t* totals, hipStream_t stream);
-hipError_t launch_calibrate_update(float* theta, const float* q_draft, const int32_t* accepted,
+hipError_t launch_calibrate_update(float* theta, const float* q_draft, const float* q_entropy,
+                                   const float* q_max, const int32_t* accepted,
                                    const int32_t* cu_rows, int n_req, int k_max, float lr,
                                    int32_t* count_out, hipStream_t stream);
-hipError_t launch_calibrate_predict(const float* theta, const float* q_draft, int n_req,
+hipError_t launch_calibrate_predict(const float* theta, const float* q_draft,
+                                    const float* q_entropy, const float* q_max, int n_req,
                                     int k_max, float* conf, hipStream_t stream);
 
 hipError_t launch_philox_uniforms(uint64_t seed, uint64_t step, int n_req, int n_pos, float* u,

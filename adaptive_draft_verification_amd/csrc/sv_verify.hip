@@ -122,19 +122,43 @@ struct Vec<SV_F32> {
 };
 
 
-// Merge two (offset, sum) pairs: both sums re-expressed against the larger offset.
+// Merge two (offset, sum) pairs: both sums re-expressed against the larger
+// offset.  The fused multiply-add is spelled out so that every caller rounds
+// alike (the compiler may otherwise fuse either product).
 __device__ __forceinline__ void merge_as(float& a, float& s, float a2, float s2) {
     const float m = fmaxf(a, a2);
-    s = s * fast_exp2(a - m) + s2 * fast_exp2(a2 - m);
+    s = fmaf(s, fast_exp2(a - m), s2 * fast_exp2(a2 - m));
     a = m;
 }
+
+// Draft-row features carry e = sum_x 2^(t_x) t_x, t_x = y_x - a, next to the
+// (offset a, sum s) pair; moving the offset from a to m turns e into
+// 2^(a - m) (e + (a - m) s).  s and a come out bit for bit as in merge_as.
+__device__ __forceinline__ void merge_ase(float& a, float& s, float& e, float a2, float s2,
+                                          float e2) {
+    const float m = fmaxf(a, a2);
+    const float f1 = fast_exp2(a - m), f2 = fast_exp2(a2 - m);
+    e = fmaf(f1, fmaf(a - m, s, e), f2 * fmaf(a2 - m, s2, e2));
+    s = fmaf(s, f1, s2 * f2);
+    a = m;
+}
+
+// Lower clamp of t in the entropy term: an id of logit -inf has weight 0 and
+// must add 0, not 0 * -inf.
+constexpr float kTFloor = -256.0f;
+
+// Feature side of a part: e (above) and the part's largest logit.
+struct FeatAcc {
+    float e = 0.0f;
+    float mx = -__builtin_inff();
+};
 
 // Exact two-pass statistics (fallback): offset = max * c, then the sum.  A
 // range holding a NaN or +inf returns S = NaN; one whose logits are all -inf
 // returns (A, S) = (-inf, 0).
-template <sv_dtype DT>
+template <sv_dtype DT, bool FEAT = false>
 __device__ void row_stats_exact(const char* row, int vocab, float c, float* red, float* out_a,
-                                float* out_s) {
+                                float* out_s, FeatAcc* feat = nullptr) {
     using V = Vec<DT>;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -170,21 +194,40 @@ __device__ void row_stats_exact(const char* row, int vocab, float c, float* red,
         return;
     }
     const float a = mx * c;
-    float s = 0.0f;
-    for (int e = tid; e < vocab; e += kThreads) s += fast_exp2(fmaf(V::load1(row, e), c, -a));
+    float s = 0.0f, ef = 0.0f;
+    for (int e = tid; e < vocab; e += kThreads) {
+        const float t = fmaf(V::load1(row, e), c, -a);
+        const float w = fast_exp2(t);
+        s += w;
+        if (FEAT) ef = fmaf(w, fmaxf(t, kTFloor), ef);
+    }
     s = wave_sum(s);
-    if (lane == 0) red[wave] = s;
+    if (FEAT) ef = wave_sum(ef);
+    if (lane == 0) {
+        red[2 * wave] = s;
+        red[2 * wave + 1] = ef;
+    }
     __syncthreads();
-    float tot = red[0];
-    for (int w = 1; w < kThreads / kWave; ++w) tot += red[w];
+    float tot = red[0], etot = red[1];
+    for (int w = 1; w < kThreads / kWave; ++w) {
+        tot += red[2 * w];
+        etot += red[2 * w + 1];
+    }
     *out_a = a;
     *out_s = tot;
+    if (FEAT) {
+        feat->e = etot;
+        feat->mx = mx;
+    }
 }
 
-// One-pass row statistics; returns through out_a/out_s (identical in every thread).
-template <sv_dtype DT>
+// One-pass row statistics; returns through out_a/out_s (identical in every
+// thread).  FEAT also accumulates the entropy term and the largest logit (two
+// more VALU operations per element) into *feat; (a, s) come out bit for bit
+// as without it.
+template <sv_dtype DT, bool FEAT = false>
 __device__ void row_stats_stochastic(const char* row, int vocab, float c, float* red,
-                                     float* out_a, float* out_s) {
+                                     float* out_a, float* out_s, FeatAcc* feat = nullptr) {
     using V = Vec<DT>;
     using raw_t = typename V::raw_t;
     constexpr int E = V::kElems;
@@ -194,10 +237,24 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
     const int nvec = aligned ? vocab / E : 0;
     const raw_t* vrow = reinterpret_cast<const raw_t*>(row);
 
-    float acc[E];
+    float acc[E], eacc[E];
 #pragma unroll
-    for (int k = 0; k < E; ++k) acc[k] = 0.0f;
+    for (int k = 0; k < E; ++k) {
+        acc[k] = 0.0f;
+        eacc[k] = 0.0f;
+    }
+    float mx = -kInf;
     float a_t = 0.0f;
+    // one element: its weight into acc, and with FEAT its entropy term and max
+    auto add = [&](float x, int k) {
+        const float t = fmaf(x, c, -a_t);
+        const float w = fast_exp2(t);
+        acc[k] += w;
+        if (FEAT) {
+            eacc[k] = fmaf(w, fmaxf(t, kTFloor), eacc[k]);
+            mx = fmaxf(mx, x);
+        }
+    };
     int i = tid;
     if (i < nvec) {
         float x[E];
@@ -207,7 +264,7 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         for (int k = 1; k < E; ++k) m = fmaxf(m, x[k]);
         a_t = (m == -kInf) ? 0.0f : m * c;
 #pragma unroll
-        for (int k = 0; k < E; ++k) acc[k] += fast_exp2(fmaf(x[k], c, -a_t));
+        for (int k = 0; k < E; ++k) add(x[k], k);
         i += kThreads;
     } else {
         const int e = nvec * E + tid;
@@ -225,38 +282,61 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
             float x[E];
             V::unpack(w[u], x);
 #pragma unroll
-            for (int k = 0; k < E; ++k) acc[k] += fast_exp2(fmaf(x[k], c, -a_t));
+            for (int k = 0; k < E; ++k) add(x[k], k);
         }
     }
     for (; i < nvec; i += kThreads) {
         float x[E];
         V::unpack(stream_load(vrow + i), x);
 #pragma unroll
-        for (int k = 0; k < E; ++k) acc[k] += fast_exp2(fmaf(x[k], c, -a_t));
+        for (int k = 0; k < E; ++k) add(x[k], k);
     }
-    for (int e = nvec * E + tid; e < vocab; e += kThreads)
-        acc[0] += fast_exp2(fmaf(V::load1(row, e), c, -a_t));
+    for (int e = nvec * E + tid; e < vocab; e += kThreads) add(V::load1(row, e), 0);
 
-    float s = 0.0f;
+    float s = 0.0f, ef = 0.0f;
 #pragma unroll
-    for (int k = 0; k < E; ++k) s += acc[k];
+    for (int k = 0; k < E; ++k) {
+        s += acc[k];
+        if (FEAT) ef += eacc[k];
+    }
 
     float a = a_t;
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) {
         const float a2 = __shfl_xor(a, o), s2 = __shfl_xor(s, o);
-        merge_as(a, s, a2, s2);
+        if (FEAT) {
+            merge_ase(a, s, ef, a2, s2, __shfl_xor(ef, o));
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+        } else {
+            merge_as(a, s, a2, s2);
+        }
     }
     if (lane == 0) {
-        red[2 * wave] = a;
-        red[2 * wave + 1] = s;
+        red[4 * wave] = a;
+        red[4 * wave + 1] = s;
+        if (FEAT) {
+            red[4 * wave + 2] = ef;
+            red[4 * wave + 3] = mx;
+        }
     }
     __syncthreads();
-    float A = red[0], S = red[1];
-    for (int w = 1; w < kThreads / kWave; ++w) merge_as(A, S, red[2 * w], red[2 * w + 1]);
+    float A = red[0], S = red[1], EF = FEAT ? red[2] : 0.0f, MX = FEAT ? red[3] : -kInf;
+    for (int w = 1; w < kThreads / kWave; ++w) {
+        if (FEAT) {
+            merge_ase(A, S, EF, red[4 * w], red[4 * w + 1], red[4 * w + 2]);
+            MX = fmaxf(MX, red[4 * w + 3]);
+        } else {
+            merge_as(A, S, red[4 * w], red[4 * w + 1]);
+        }
+    }
     __syncthreads();
-    if (!(S > 0.0f) || !is_finite_bits(S) || !is_finite_bits(A)) {
-        row_stats_exact<DT>(row, vocab, c, red, &A, &S);  // block-uniform branch
+    if (!(S > 0.0f) || !is_finite_bits(S) || !is_finite_bits(A) ||
+        (FEAT && !is_finite_bits(EF))) {
+        // block-uniform branch
+        row_stats_exact<DT, FEAT>(row, vocab, c, red, &A, &S, feat);
+    } else if (FEAT) {
+        feat->e = EF;
+        feat->mx = MX;
     }
     *out_a = A;
     *out_s = S;
@@ -287,13 +367,12 @@ __device__ void row_argmax(const char* row, int vocab, float* redf, int* redi, f
         for (int u = 0; u < kUnroll; ++u) {
             float x[E];
             V::unpack(w[u], x);
+            // IEEE maximum propagates NaN (v_maximum3_f32), so one test per
+            // chunk finds a NaN; a NaN chunk never beats the running max
             float cm = x[0];
 #pragma unroll
-            for (int k = 1; k < E; ++k) {
-                cm = fmaxf(cm, x[k]);
-                nan |= x[k] != x[k];
-            }
-            nan |= x[0] != x[0];
+            for (int k = 1; k < E; ++k) cm = __builtin_elementwise_maximum(cm, x[k]);
+            nan |= cm != cm;
             if (cm > best) {
                 best = cm;
                 int pos = E - 1;
@@ -376,6 +455,13 @@ struct alignas(16) PartStat {
     float zd;
     int32_t idx;
 };
+// Draft-row features of one part (stochastic mode, when asked for):
+//   e  : sum_x 2^(t_x) t_x, t_x = z_x * log2(e)/T - a (a the part's offset);
+//   mx : the part's largest logit.
+struct alignas(8) FeatPart {
+    float e;
+    float mx;
+};
 constexpr int kMaxParts = 8;
 #ifndef SV_PART_IDS
 #define SV_PART_IDS 65536
@@ -404,11 +490,14 @@ struct Args {
     uint64_t seed;
     uint64_t step;
     PartStat* stats;  // [n, 2*k_max + 1, kMaxParts]
+    FeatPart* feat;   // [n, k_max, kMaxParts] (draft rows)
     int32_t* out_tokens;
     int32_t* out_accepted;
     float* out_p;
     float* out_q;
     float* out_resid;
+    float* out_qh;    // draft-row entropy (bits), or null
+    float* out_qm;    // draft-row largest probability, or null
     int32_t* dev_error;
 };
 
@@ -712,6 +801,8 @@ __device__ void emit_fault(const Args& a, int r, int bits) {
     for (int j = tid; j < a.k_max; j += blockDim.x) {
         if (a.out_p) a.out_p[(int64_t)r * a.k_max + j] = -1.0f;
         if (a.out_q) a.out_q[(int64_t)r * a.k_max + j] = -1.0f;
+        if (a.out_qh) a.out_qh[(int64_t)r * a.k_max + j] = -1.0f;
+        if (a.out_qm) a.out_qm[(int64_t)r * a.k_max + j] = -1.0f;
     }
     if (tid == 0) {
         a.out_accepted[r] = -1;
@@ -726,13 +817,15 @@ struct RowMerged {
     float pd, lpd;   // stochastic: p(d) and log2 p(d) of the position's draft id
     float mx;        // greedy: the row's max logit
     int idx;         // greedy: lowest id reaching it
+    float ent, pmax; // stochastic draft row with features: entropy (bits), largest probability
     bool fault;      // NaN or +inf somewhere, or no finite mass
 };
 
 // Merge the parts of one row in part order (deterministic).  d: the draft id
-// whose probability is wanted, or -1.
+// whose probability is wanted, or -1.  fs: the row's feature records, or null.
 template <bool GREEDY>
-__device__ RowMerged merge_parts(const PartStat* ps, int parts, int plen, int d, float c) {
+__device__ RowMerged merge_parts(const PartStat* ps, int parts, int plen, int d, float c,
+                                 const FeatPart* fs = nullptr) {
     PartStat p[kMaxParts];
 #pragma unroll
     for (int h = 0; h < kMaxParts; ++h)
@@ -744,6 +837,8 @@ __device__ RowMerged merge_parts(const PartStat* ps, int parts, int plen, int d,
     m.lpd = -kInf;
     m.mx = -kInf;
     m.idx = 0x7fffffff;
+    m.ent = -1.0f;
+    m.pmax = -1.0f;
     m.fault = false;
     if (GREEDY) {
 #pragma unroll
@@ -785,6 +880,22 @@ __device__ RowMerged merge_parts(const PartStat* ps, int parts, int plen, int d,
         m.pd = exp2f(y) / m.S;
         m.lpd = y - log2f(m.S);
     }
+    if (fs != nullptr && !m.fault) {
+        // entropy = log2 S - E / S with E = sum_x 2^(y_x - A) (y_x - A): each
+        // part's e moved to the row's offset A (parts without mass add nothing)
+        float e = 0.0f, mx = -kInf;
+#pragma unroll
+        for (int h = 0; h < kMaxParts; ++h) {
+            if (h >= parts) break;
+            if (p[h].s > 0.0f) {
+                const FeatPart f = fs[h];
+                e += fast_exp2(p[h].a - m.A) * fmaf(p[h].a - m.A, p[h].s, f.e);
+                mx = fmaxf(mx, f.mx);
+            }
+        }
+        m.ent = fmaxf(0.0f, log2f(m.S) - e / m.S);
+        m.pmax = exp2f(fmaf(mx, c, -m.A)) / m.S;
+    }
     return m;
 }
 
@@ -792,6 +903,7 @@ struct FinishSmem {
     DrawSmem draw;
     float ta[kWave], ts[kWave], qa[kWave], qs[kWave];  // merged rows of position j
     float tpd[kWave], qpd[kWave];                      // p(d_j), q(d_j)
+    float qh[kWave], qm[kWave];                        // draft row j's features
     int gidx[kWave];                                   // greedy: argmax of target row j
     float ba, bs;                                      // bonus row b (stochastic)
     int bidx;                                          // bonus row b (greedy)
@@ -827,9 +939,10 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
                     acc = t.idx == d;
                     sm.gidx[j] = t.idx;
                 } else {
+                    const bool feat = a.out_qh != nullptr || a.out_qm != nullptr;
                     const RowMerged q = merge_parts<false>(
                         st + (int64_t)(k_max + 1 + j) * kMaxParts, parts, plen, d_ok ? d : -1,
-                        a.c);
+                        a.c, feat ? a.feat + ((int64_t)r * k_max + j) * kMaxParts : nullptr);
                     if (q.fault) fault |= SV_DEV_NONFINITE;
                     float u, v;
                     draw_uniforms(a.seed, a.step, (uint32_t)r, (uint32_t)j, &u, &v);
@@ -842,6 +955,8 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
                     sm.qs[j] = q.S;
                     sm.tpd[j] = t.pd;
                     sm.qpd[j] = q.pd;
+                    sm.qh[j] = q.ent;
+                    sm.qm[j] = q.pmax;
                 }
             }
             if (lane == 0) {
@@ -904,13 +1019,17 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
         tok_out[j] = t;
     }
     for (int j = tid; j < k_max; j += blockDim.x) {
-        float p = -1.0f, q = -1.0f;
+        float p = -1.0f, q = -1.0f, qh = -1.0f, qm = -1.0f;
         if (!GREEDY && j < b) {
             p = sm.tpd[j];
             q = sm.qpd[j];
+            qh = sm.qh[j];
+            qm = sm.qm[j];
         }
         if (a.out_p) a.out_p[(int64_t)r * k_max + j] = p;
         if (a.out_q) a.out_q[(int64_t)r * k_max + j] = q;
+        if (a.out_qh) a.out_qh[(int64_t)r * k_max + j] = qh;
+        if (a.out_qm) a.out_qm[(int64_t)r * k_max + j] = qm;
     }
     if (tid == 0) {
         a.out_accepted[r] = L;
@@ -954,9 +1073,9 @@ __device__ __forceinline__ void pass1_slot(int g, int n_req, int k_max, bool gre
 #endif
 }
 
-template <sv_dtype DT, bool GREEDY>
+template <sv_dtype DT, bool GREEDY, bool FEAT>
 __global__ __launch_bounds__(kThreads) void rowstats_kernel(Args a, int n_req, int parts) {
-    __shared__ float redf[2 * (kThreads / kWave)];
+    __shared__ float redf[4 * (kThreads / kWave)];
     __shared__ int redi[2 * (kThreads / kWave)];
     const int h = blockIdx.x % parts;
     int r, slot;
@@ -993,7 +1112,17 @@ __global__ __launch_bounds__(kThreads) void rowstats_kernel(Args a, int n_req, i
     float zd = 0.0f;
     if (threadIdx.x == 0 && want_zd) zd = Vec<DT>::load1(row, d);
     float A, S;
-    row_stats_stochastic<DT>(prow, p1 - p0, a.c, redf, &A, &S);
+    FeatAcc fa;
+    if (FEAT && is_draft)
+        row_stats_stochastic<DT, true>(prow, p1 - p0, a.c, redf, &A, &S, &fa);
+    else
+        row_stats_stochastic<DT>(prow, p1 - p0, a.c, redf, &A, &S);
+    if (FEAT && is_draft && threadIdx.x == 0) {
+        FeatPart f;
+        f.e = fa.e;
+        f.mx = fa.mx;
+        a.feat[((int64_t)r * a.k_max + j) * kMaxParts + h] = f;
+    }
     if (threadIdx.x == 0) {
         // S is NaN or +inf for a faulty part, 0 (A = -inf) for one without mass
         const bool fault = !(S >= 0.0f) || !is_finite_bits(S) || (S > 0.0f && !is_finite_bits(A));
@@ -1012,6 +1141,10 @@ __global__ __launch_bounds__(GREEDY ? kWave : kP2Threads) void decide_kernel(Arg
     finish_request<DT, GREEDY>(a, blockIdx.x, fin);
 }
 
+size_t stats_bytes(int n_req, int k_max) {
+    return (size_t)n_req * (size_t)(2 * k_max + 1) * kMaxParts * sizeof(PartStat);
+}
+
 int host_row_parts(int vocab) {
     const int h = (vocab + kPartIds - 1) / kPartIds;
     return h < 1 ? 1 : (h > kMaxParts ? kMaxParts : h);
@@ -1020,17 +1153,28 @@ int host_row_parts(int vocab) {
 template <sv_dtype DT, bool GREEDY>
 hipError_t launch_typed(const VerifyArgs& v, hipStream_t stream) {
     const int esize = Vec<DT>::kBytes;
+    // draft-row features exist only where draft rows are read (stochastic)
+    const bool feat = !GREEDY && (v.out_q_entropy != nullptr || v.out_q_max != nullptr);
     Args a{static_cast<const char*>(v.target), v.target_ld * esize, v.target_rows,
            static_cast<const char*>(v.draft), v.draft_ld * esize, v.vocab, v.draft_tokens,
            v.cu_rows, v.k_max, kLog2e / v.temperature, v.seed, v.step,
-           static_cast<PartStat*>(v.ws), v.out_tokens, v.out_accepted, v.out_p_draft,
-           v.out_q_draft, v.out_residual_mass, v.dev_error};
+           static_cast<PartStat*>(v.ws),
+           reinterpret_cast<FeatPart*>(static_cast<char*>(v.ws) + stats_bytes(v.n_req, v.k_max)),
+           v.out_tokens, v.out_accepted, v.out_p_draft, v.out_q_draft, v.out_residual_mass,
+           v.out_q_entropy, v.out_q_max, v.dev_error};  // greedy: -1 written there
     const int slots = GREEDY ? v.k_max + 1 : 2 * v.k_max + 1;
     if (v.stages & 1) {
         const int parts = host_row_parts(v.vocab);
-        hipLaunchKernelGGL((rowstats_kernel<DT, GREEDY>),
-                           dim3((unsigned)(v.n_req * slots * parts)), dim3(kThreads), 0, stream, a,
-                           v.n_req, parts);
+        const dim3 grid((unsigned)(v.n_req * slots * parts));
+        if constexpr (GREEDY)
+            hipLaunchKernelGGL((rowstats_kernel<DT, true, false>), grid, dim3(kThreads), 0, stream,
+                               a, v.n_req, parts);
+        else if (feat)
+            hipLaunchKernelGGL((rowstats_kernel<DT, false, true>), grid, dim3(kThreads), 0, stream,
+                               a, v.n_req, parts);
+        else
+            hipLaunchKernelGGL((rowstats_kernel<DT, false, false>), grid, dim3(kThreads), 0,
+                               stream, a, v.n_req, parts);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1054,7 +1198,7 @@ __global__ void philox_uniforms_kernel(uint64_t seed, uint64_t step, int n_req, 
 }  // namespace
 
 size_t verify_workspace_bytes(int n_req, int k_max) {
-    return (size_t)n_req * (size_t)(2 * k_max + 1) * kMaxParts * sizeof(PartStat);
+    return stats_bytes(n_req, k_max) + (size_t)n_req * (size_t)k_max * kMaxParts * sizeof(FeatPart);
 }
 
 hipError_t launch_verify(const VerifyArgs& v, hipStream_t stream) {

@@ -21,8 +21,10 @@ the HBM bytes the byte counters measured for it
 (profiles/, while the kernel's sources are unchanged); pass 2's bytes (the
 rows each draw reads again) are reported beside it.  A second leg verifies
 every draft (full K: 2048 target + 1792 draft rows) for the bandwidth figure
-at the largest size.  The CPU oracle runs whole steps of the same workload on
-the host for the cpu_baseline figure.
+at the largest size.  Two smaller legs time pass 1 with the draft-row
+features (entropy, largest probability) accumulated as well, and the one-K-
+per-batch selection (sv_uniform_k_select).  The CPU oracle runs whole steps of
+the same workload on the host for the cpu_baseline figure.
 
 Prints one JSON line.
 """
@@ -293,21 +295,26 @@ def main():
     _, stage_ms = timed(args.steps)
     p2_rows = pass2_rows(range(args.steps), kept_h)
 
-    def pass1_launch_ms(iters, reps=None, cu_rows=None):
+    def pass1_launch_ms(iters, reps=None, cu_rows=None, features=False):
         """Mean duration of the roofline kernel: `iters` pass-1 launches back to
-        back (replicas alternating) between two events on the launch stream."""
+        back (replicas alternating) between two events on the launch stream.
+        features: the launch that also accumulates the draft-row features."""
         reps = reps or replicas
         cu_i = cu if cu_rows is None else cu_rows
+        fkw = {}
+        if features:
+            fkw = dict(out_q_entropy=torch.empty(n, K, dtype=torch.float32, device=dev),
+                       out_q_max=torch.empty(n, K, dtype=torch.float32, device=dev))
         for i in range(2):
             tp_, dr_ = reps[i % len(reps)]
             sv.sv_verify_stages(tp_, dr_, toks_d, cu_i, mode, w.tau, w.seed, i, tok_out,
-                                acc_out, ws, 1, p_out, q_out, res_out, err, vocab=V)
+                                acc_out, ws, 1, p_out, q_out, res_out, err, vocab=V, **fkw)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(iters):
             tp_, dr_ = reps[i % len(reps)]
             sv.sv_verify_stages(tp_, dr_, toks_d, cu_i, mode, w.tau, w.seed, i, tok_out,
-                                acc_out, ws, 1, p_out, q_out, res_out, err, vocab=V)
+                                acc_out, ws, 1, p_out, q_out, res_out, err, vocab=V, **fkw)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / iters
@@ -352,6 +359,15 @@ def main():
             "verify_rows_per_s": round(rows_tf / ((f1 + f2) * 1e-3), 1),
             "iters": args.full_k_iters,
         }
+
+    # -------------------------------------------- draft-row features leg
+    # pass 1 asked for the draft rows' entropy and largest probability as well
+    features = None
+    if mode == sv.SV_STOCHASTIC:
+        feat_ms = pass1_launch_ms(args.steps, features=True)
+        features = {"pass1_us": round(feat_ms * 1e3, 2),
+                    "pass1_gbps": round(pass1_bytes / (feat_ms * 1e-3) / 1e9, 1),
+                    "vs_plain_pass1": round(feat_ms / roof_ms, 4)}
 
     # ------------------------------------------------ uniform draft length leg
     # the DSD-style alternative to the adaptive budget: one K for the batch
@@ -428,6 +444,7 @@ def main():
         "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 4),
         "step_hbm_gbps": round((pass1_bytes + pass2_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
         "uniform_k": uniform_k,
+        "draft_features": features,
         "full_k": full,
         "cpu_baseline": cpu,
     }

@@ -70,7 +70,8 @@ const char* sv_status_str(sv_status s);
 
 /*
  * Workspace bytes the device calls need (0 = none; pass ws = NULL then).
- * sv_verify keeps one 16-byte statistics record per candidate row.
+ * sv_verify keeps one 16-byte statistics record per candidate row part and
+ * one 8-byte feature record per draft row part.
  */
 size_t sv_budget_workspace_bytes(int32_t n_req, int32_t k_max);
 size_t sv_verify_workspace_bytes(int32_t n_req, int32_t k_max);
@@ -242,15 +243,26 @@ sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
  *                -1 elsewhere and in greedy mode; may be NULL.
  * out_residual_mass: [n_req] fp32 sum max(0, p_L - q_L) when a draft was
  *                rejected in stochastic mode, else -1; may be NULL.
+ * out_q_entropy, out_q_max: [n_req, k_max] fp32 draft-row features for
+ *                acceptance prediction (same page, section "켜는 방법과
+ *                제약": a drafter without a confidence head gets its
+ *                estimates from a small model over its logits): the entropy
+ *                in bits, -sum_x q_j(x) log2 q_j(x), and the largest
+ *                probability max_x q_j(x) of draft row j, for j < b in
+ *                stochastic mode; -1 elsewhere and in greedy mode (draft rows
+ *                are not read there).  May be NULL; when either is given,
+ *                pass 1 accumulates them while it streams the draft rows.
  * A faulty request (any SV_DEV_* bit of its own) writes -1 to all of its
  * outputs.
- * ws:            sv_verify_workspace_bytes(n_req, k_max) bytes (per-row
- *                statistics passed from the first launch to the second).
- *                Calls that overlap in time must not share a workspace.
- * Launch: two kernels.  Pass 1: one 256-thread workgroup per candidate row
- * (n_req * (2*k_max + 1) stochastic, n_req * (k_max + 1) greedy; rows beyond
- * a request's kept count do nothing).  Pass 2: one workgroup per request
- * (1024 threads stochastic, 64 greedy) decides and draws.
+ * ws:            sv_verify_workspace_bytes(n_req, k_max) bytes (per-part
+ *                row statistics and draft-row feature sums passed from the
+ *                first launch to the second).  Calls that overlap in time
+ *                must not share a workspace.
+ * Launch: two kernels.  Pass 1: one 512-thread workgroup per candidate row
+ * part, rows cut into ceil(vocab / 65536) <= 8 parts (n_req * (2*k_max + 1)
+ * rows stochastic, n_req * (k_max + 1) greedy; rows beyond a request's kept
+ * count do nothing).  Pass 2: one workgroup per request (1024 threads
+ * stochastic, 64 greedy) merges the parts, decides and draws.
  * Errors: SV_ERR_NULL; SV_ERR_DTYPE; SV_ERR_SHAPE if n_req < 0, k_max outside
  * [0, SV_MAX_DRAFT], vocab outside [1, SV_MAX_VOCAB], a stride below vocab or
  * target_rows < 0; SV_ERR_VALUE for an unknown mode or a bad temperature;
@@ -261,17 +273,19 @@ sv_status sv_verify(const void* target_logits, int64_t target_ld, int64_t target
                     const int32_t* draft_tokens, const int32_t* cu_rows, int32_t n_req,
                     int32_t k_max, sv_mode mode, float temperature, uint64_t seed, uint64_t step,
                     int32_t* out_tokens, int32_t* out_accepted, float* out_p_draft,
-                    float* out_q_draft, float* out_residual_mass, int32_t* dev_error, void* ws,
-                    size_t ws_bytes, void* stream);
+                    float* out_q_draft, float* out_residual_mass, float* out_q_entropy,
+                    float* out_q_max, int32_t* dev_error, void* ws, size_t ws_bytes,
+                    void* stream);
 
 /*
  * sv_verify_stages — sv_verify split at its two launches, for callers that
  * time or schedule the passes on their own.  Same arguments and checks as
  * sv_verify, plus `stages`: 1 = pass 1 only (row statistics into ws),
  * 2 = pass 2 only (decisions, draws and outputs from the ws that a pass 1
- * with the same arguments filled earlier on the same stream), 3 = both
- * (identical to sv_verify).  Errors: as sv_verify; SV_ERR_VALUE if stages is
- * not 1, 2 or 3.
+ * with the same arguments filled earlier on the same stream; the draft-row
+ * features are read back only if that pass 1 was asked for them too), 3 =
+ * both (identical to sv_verify).  Errors: as sv_verify; SV_ERR_VALUE if
+ * stages is not 1, 2 or 3.
  */
 sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t target_rows,
                            const void* draft_logits, int64_t draft_ld, sv_dtype dtype,
@@ -279,8 +293,9 @@ sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t
                            int32_t n_req, int32_t k_max, sv_mode mode, float temperature,
                            uint64_t seed, uint64_t step, int32_t* out_tokens,
                            int32_t* out_accepted, float* out_p_draft, float* out_q_draft,
-                           float* out_residual_mass, int32_t* dev_error, void* ws,
-                           size_t ws_bytes, int32_t stages, void* stream);
+                           float* out_residual_mass, float* out_q_entropy, float* out_q_max,
+                           int32_t* dev_error, void* ws, size_t ws_bytes, int32_t stages,
+                           void* stream);
 
 /*
  * Acceptance statistics and online calibration of the per-position
@@ -312,28 +327,39 @@ sv_status sv_accept_stats(const int32_t* accepted, const int32_t* cu_rows, int32
                           uint64_t* totals, void* stream);
 
 /*
- * sv_calibrate_update — one gradient step of the logistic acceptance model
- *   c_j = sigmoid(alpha_j + beta * x),  x = log2 q(d_j) clamped to [-64, 0]
- * (q <= 0 or NaN reads as -64), theta = [alpha_0 .. alpha_{k_max-1}, beta]
- * (device fp32 [k_max + 1], updated in place), on the mean log-loss of the
- * verified positions: theta -= lr * grad / N.  q_draft: [n_req, k_max] fp32,
- * sv_verify's out_q_draft.  count_out: [1] int32, N (or NULL).  One
- * workgroup; fixed-order reductions (deterministic).  Errors: SV_ERR_SHAPE,
- * SV_ERR_NULL, SV_ERR_VALUE (lr negative or not finite).
+ * The logistic acceptance model over three features of draft row j of
+ * request r, all reported by sv_verify:
+ *   c_j = sigmoid(alpha_j + beta_1 x_1 + beta_2 x_2 + beta_3 x_3),
+ *   x_1 = log2 q_j(d_j) clamped to [-64, 0] (q <= 0 or NaN reads as -64),
+ *   x_2 = the row's entropy in bits clamped to [0, 64],
+ *   x_3 = the row's largest probability clamped to [0, 1]
+ * (NaN or a negative value reads as 0 for x_2 and x_3, and so does a feature
+ * array passed as NULL).  theta = [alpha_0 .. alpha_{k_max-1}, beta_1,
+ * beta_2, beta_3]: device fp32 [k_max + 3].
+ * q_draft, q_entropy, q_max: [n_req, k_max] fp32, sv_verify's out_q_draft,
+ * out_q_entropy and out_q_max (q_entropy and q_max may be NULL).
  */
-sv_status sv_calibrate_update(float* theta, const float* q_draft, const int32_t* accepted,
+
+/*
+ * sv_calibrate_update — one gradient step of the model on the mean log-loss
+ * of the verified positions: theta -= lr * grad / N (theta updated in
+ * place).  count_out: [1] int32, N (or NULL).  One workgroup; fixed-order
+ * reductions (deterministic).  Errors: SV_ERR_SHAPE, SV_ERR_NULL,
+ * SV_ERR_VALUE (lr negative or not finite).
+ */
+sv_status sv_calibrate_update(float* theta, const float* q_draft, const float* q_entropy,
+                              const float* q_max, const int32_t* accepted,
                               const int32_t* cu_rows, int32_t n_req, int32_t k_max, float lr,
                               int32_t* count_out, void* stream);
 
 /*
- * sv_calibrate_predict — conf[r, j] = sigmoid(alpha_j + beta * x(q[r, j])):
- * the per-position acceptance estimates sv_budget_select and
- * sv_uniform_k_select read, from the drafter's probabilities of its own
- * tokens.  q_draft, conf: [n_req, k_max] fp32.  Errors: SV_ERR_SHAPE,
- * SV_ERR_NULL.
+ * sv_calibrate_predict — conf[r, j] = c_j of request r: the per-position
+ * acceptance estimates sv_budget_select and sv_uniform_k_select read.
+ * conf: [n_req, k_max] fp32.  Errors: SV_ERR_SHAPE, SV_ERR_NULL.
  */
-sv_status sv_calibrate_predict(const float* theta, const float* q_draft, int32_t n_req,
-                               int32_t k_max, float* conf, void* stream);
+sv_status sv_calibrate_predict(const float* theta, const float* q_draft, const float* q_entropy,
+                               const float* q_max, int32_t n_req, int32_t k_max, float* conf,
+                               void* stream);
 
 /*
  * sv_philox_uniforms — the (u, v) pairs sv_verify draws, for inspection.

@@ -20,7 +20,11 @@ Comparison rules:
   GPU's id must carry positive weight;
 * a residual whose oracle mass is below the mass floor (1e-7) is empty to
   fp32, so the zero-mass fallback (a draw from p at that row) may apply: the
-  GPU's id then only has to lie in p's support.
+  GPU's id then only has to lie in p's support;
+* draft-row features: the largest probability relative 1e-5 (the same
+  exp2-over-sum shape as q(d), never subnormal: it is at least 1/V); the
+  entropy in bits absolute 1e-4 plus relative 1e-5 (log2 S minus a ratio of
+  fp32 sums whose per-thread offsets are merged with a few roundings each).
 """
 
 import numpy as np
@@ -35,6 +39,8 @@ CDF_BAND = 1e-5
 P_RTOL = 1e-5
 RESID_ATOL = 1e-7
 P_ATOL = 2.0 ** -148  # two fp32 subnormal ulps
+H_ATOL = 1e-4         # bits
+H_RTOL = 1e-5
 
 
 def dev():
@@ -103,11 +109,12 @@ def check_pack(kept, last_token, draft_tokens, k_max):
 # ------------------------------------------------------------------ verify
 
 def gpu_verify(target, draft, draft_tokens, cu_rows, k_max, mode, tau, dtype, seed=0, step=0,
-               vocab=None, target_ld=None, draft_ld=None):
+               vocab=None, target_ld=None, draft_ld=None, features=False):
     """Run sv_verify on host arrays (fp32 holding the exact logit values).
 
     target_ld / draft_ld > vocab place rows at a wider stride (the extra
-    columns hold NaN that must never be read)."""
+    columns hold NaN that must never be read).  features: also ask for the
+    draft-row features."""
     V = target.shape[1] if vocab is None else vocab
 
     def widen(a, ld):
@@ -122,7 +129,7 @@ def gpu_verify(target, draft, draft_tokens, cu_rows, k_max, mode, tau, dtype, se
     out = sv.verify(t, d, to_dev(np.asarray(draft_tokens, np.int32)),
                     to_dev(np.asarray(cu_rows, np.int32)),
                     sv.SV_GREEDY if mode == "greedy" else sv.SV_STOCHASTIC, tau, seed, step,
-                    vocab=V)
+                    vocab=V, features=features)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -136,11 +143,14 @@ def compare_verify(g, target, draft, draft_tokens, cu_rows, k_max, vocab, mode, 
     assert int(g["dev_error"][0]) == o["dev_error"], (int(g["dev_error"][0]), o["dev_error"])
     n = len(cu_rows) - 1
     draft_tokens = np.asarray(draft_tokens).reshape(n, k_max)
+    feats = "q_entropy" in g
     if mode == "greedy":
         np.testing.assert_array_equal(g["tokens"], o["tokens"])
         np.testing.assert_array_equal(g["accepted"], o["accepted"])
         assert (g["p_draft"] == -1).all() and (g["q_draft"] == -1).all()
         assert (g["residual_mass"] == -1).all()
+        if feats:
+            assert (g["q_entropy"] == -1).all() and (g["q_max"] == -1).all()
         return stats
     for r in range(n):
         res = o["per_request"][r]
@@ -148,6 +158,8 @@ def compare_verify(g, target, draft, draft_tokens, cu_rows, k_max, vocab, mode, 
             assert g["accepted"][r] == -1 and (g["tokens"][r] == -1).all()
             assert (g["p_draft"][r] == -1).all() and (g["q_draft"][r] == -1).all()
             assert g["residual_mass"][r] == -1
+            if feats:
+                assert (g["q_entropy"][r] == -1).all() and (g["q_max"][r] == -1).all()
             continue
         b = int(cu_rows[r + 1] - cu_rows[r] - 1)
         # probabilities of the draft ids
@@ -156,6 +168,12 @@ def compare_verify(g, target, draft, draft_tokens, cu_rows, k_max, vocab, mode, 
         np.testing.assert_allclose(g["q_draft"][r, :b], res["q_d"], rtol=P_RTOL, atol=P_ATOL,
                                    err_msg=f"q(d) request {r}")
         assert (g["p_draft"][r, b:] == -1).all() and (g["q_draft"][r, b:] == -1).all()
+        if feats:
+            np.testing.assert_allclose(g["q_entropy"][r, :b], res["q_entropy"], rtol=H_RTOL,
+                                       atol=H_ATOL, err_msg=f"entropy request {r}")
+            np.testing.assert_allclose(g["q_max"][r, :b], res["q_max"], rtol=P_RTOL, atol=0,
+                                       err_msg=f"largest probability request {r}")
+            assert (g["q_entropy"][r, b:] == -1).all() and (g["q_max"][r, b:] == -1).all()
         Lg = int(g["accepted"][r])
         assert 0 <= Lg <= b
         replayed = Lg != res["L"]

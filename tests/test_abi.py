@@ -44,7 +44,9 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    assert sv.sv_verify_workspace_bytes(256, 7) == 256 * 15 * 8 * 16  # 8 parts per row, 16 B each
+    # 8 parts per row: a 16-byte record per part of each of the 2K+1 rows, and an
+    # 8-byte feature record per part of each of the K draft rows
+    assert sv.sv_verify_workspace_bytes(256, 7) == 256 * 15 * 8 * 16 + 256 * 7 * 8 * 8
     assert sv.sv_verify_workspace_bytes(-1, 7) == 0
     # a 16-byte header, then an int32 rank and an fp32 survival per slot
     assert sv.sv_budget_workspace_bytes(256, 7) == 16 + 1792 * 8
@@ -149,8 +151,8 @@ def verify(**kw):
     args = dict(target=FAKE, target_ld=32, target_rows=16, draft=FAKE, draft_ld=32,
                 dtype=sv.SV_F32, vocab=32, draft_tokens=FAKE, cu_rows=FAKE, n_req=4, k_max=3,
                 mode=sv.SV_STOCHASTIC, temperature=1.0, seed=0, step=0, out_tokens=FAKE,
-                out_accepted=FAKE, out_p=None, out_q=None, out_resid=None, dev_error=None,
-                ws=FAKE, ws_bytes=WS43, stream=None)
+                out_accepted=FAKE, out_p=None, out_q=None, out_resid=None, out_qh=None,
+                out_qm=None, dev_error=None, ws=FAKE, ws_bytes=WS43, stream=None)
     args.update(kw)
     return sv._lib.sv_verify(*args.values())
 
@@ -186,8 +188,8 @@ def test_verify_stages_validation():
     base = dict(target=FAKE, target_ld=32, target_rows=16, draft=FAKE, draft_ld=32,
                 dtype=sv.SV_F32, vocab=32, draft_tokens=FAKE, cu_rows=FAKE, n_req=4, k_max=3,
                 mode=sv.SV_STOCHASTIC, temperature=1.0, seed=0, step=0, out_tokens=FAKE,
-                out_accepted=FAKE, out_p=None, out_q=None, out_resid=None, dev_error=None,
-                ws=FAKE, ws_bytes=WS43)
+                out_accepted=FAKE, out_p=None, out_q=None, out_resid=None, out_qh=None,
+                out_qm=None, dev_error=None, ws=FAKE, ws_bytes=WS43)
     for bad in (0, 4, -1):
         assert sv._lib.sv_verify_stages(*base.values(), bad, None) == sv.SV_ERR_VALUE
     base["ws"] = None
@@ -201,15 +203,19 @@ def test_calibration_host_validation():
     assert lib.sv_accept_stats(FAKE, FAKE, 4, 65, FAKE, FAKE, FAKE, None) == sv.SV_ERR_SHAPE
     assert lib.sv_accept_stats(FAKE, FAKE, 4, 3, FAKE, FAKE, None, None) == sv.SV_ERR_NULL
     assert lib.sv_accept_stats(None, FAKE, 4, 3, FAKE, FAKE, FAKE, None) == sv.SV_ERR_NULL
-    assert lib.sv_calibrate_update(FAKE, FAKE, FAKE, FAKE, 4, 65, 0.1, None, None) == sv.SV_ERR_SHAPE
-    assert lib.sv_calibrate_update(FAKE, FAKE, FAKE, FAKE, 4, 3, -0.1, None, None) == sv.SV_ERR_VALUE
-    assert lib.sv_calibrate_update(FAKE, FAKE, FAKE, FAKE, 4, 3, float("nan"), None,
+    upd = lambda th, q, acc, cu, n, k, lr: lib.sv_calibrate_update(th, q, None, None, acc, cu, n,
+                                                                    k, lr, None, None)
+    assert upd(FAKE, FAKE, FAKE, FAKE, 4, 65, 0.1) == sv.SV_ERR_SHAPE
+    assert upd(FAKE, FAKE, FAKE, FAKE, 4, 3, -0.1) == sv.SV_ERR_VALUE
+    assert lib.sv_calibrate_update(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 3, float("nan"), None,
                                    None) == sv.SV_ERR_VALUE
-    assert lib.sv_calibrate_update(None, FAKE, FAKE, FAKE, 4, 3, 0.1, None, None) == sv.SV_ERR_NULL
-    assert lib.sv_calibrate_update(FAKE, None, FAKE, FAKE, 4, 3, 0.1, None, None) == sv.SV_ERR_NULL
-    assert lib.sv_calibrate_predict(FAKE, FAKE, 4, 65, FAKE, None) == sv.SV_ERR_SHAPE
-    assert lib.sv_calibrate_predict(FAKE, None, 4, 3, FAKE, None) == sv.SV_ERR_NULL
-    assert lib.sv_calibrate_predict(None, None, 0, 3, None, None) == sv.SV_OK
+    assert upd(None, FAKE, FAKE, FAKE, 4, 3, 0.1) == sv.SV_ERR_NULL
+    assert upd(FAKE, None, FAKE, FAKE, 4, 3, 0.1) == sv.SV_ERR_NULL
+    assert upd(FAKE, FAKE, None, FAKE, 4, 3, 0.1) == sv.SV_ERR_NULL
+    pred = lambda th, q, n, k, conf: lib.sv_calibrate_predict(th, q, None, None, n, k, conf, None)
+    assert pred(FAKE, FAKE, 4, 65, FAKE) == sv.SV_ERR_SHAPE
+    assert pred(FAKE, None, 4, 3, FAKE) == sv.SV_ERR_NULL
+    assert pred(None, None, 0, 3, None) == sv.SV_OK
 
 
 def test_philox_host_validation():

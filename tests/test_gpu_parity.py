@@ -14,8 +14,8 @@ import torch
 import oracle
 import workloads
 
-from parity import (check_budget, check_pack, check_uniform_k, compare_verify, gpu_verify,
-                    logits_dtype, to_dev, workload_inputs)
+from parity import (H_ATOL, H_RTOL, P_RTOL, check_budget, check_pack, check_uniform_k,
+                    compare_verify, gpu_verify, logits_dtype, to_dev, workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,7 +152,7 @@ def test_pack_random(seed):
 
 # ------------------------------------------------------------------ verify
 
-def run_workload_verify(name, mode, adaptive):
+def run_workload_verify(name, mode, adaptive, features=False):
     w = workloads.make(name)
     if adaptive:
         cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
@@ -161,9 +161,10 @@ def run_workload_verify(name, mode, adaptive):
     else:
         kept = w.draft_len.copy()
     target, draft, toks, cu = workload_inputs(w, kept, mode)
-    log(f"{name} {mode} adaptive={adaptive}: rows={int(cu[-1])} V={w.vocab}")
+    log(f"{name} {mode} adaptive={adaptive} features={features}: rows={int(cu[-1])} "
+        f"V={w.vocab}")
     g = gpu_verify(target, draft, toks, cu, w.k_max, mode, w.tau, logits_dtype(w),
-                   seed=w.seed, step=w.step)
+                   seed=w.seed, step=w.step, features=features)
     stats = compare_verify(g, target, draft, toks, cu, w.k_max, w.vocab, mode, w.tau, w.seed,
                            w.step)
     log(f"  {stats}")
@@ -171,11 +172,12 @@ def run_workload_verify(name, mode, adaptive):
     return g, stats
 
 
+@pytest.mark.parametrize("features", [False, True])
 @pytest.mark.parametrize("mode", ["stochastic", "greedy"])
 @pytest.mark.parametrize("name,adaptive", [("tiny", True), ("tiny", False),
                                            ("b16_v32000", False), ("b64_v128256", True)])
-def test_verify_small_workloads(name, adaptive, mode):
-    run_workload_verify(name, mode, adaptive)
+def test_verify_small_workloads(name, adaptive, mode, features):
+    run_workload_verify(name, mode, adaptive, features)
 
 
 @pytest.mark.parametrize("mode", ["stochastic", "greedy"])
@@ -194,7 +196,31 @@ def test_verify_b256_v129280_greedy():
 
 
 def test_verify_b256_mix_v256000():
-    run_workload_verify("b256_mix_v256000", "stochastic", True)
+    run_workload_verify("b256_mix_v256000", "stochastic", True, features=True)
+
+
+def test_features_leave_the_decisions_alone():
+    """Asking for the draft-row features switches pass 1's draft rows to the
+    accumulating kernel; the row statistics, hence every decision, draw and
+    probability, must come out bit for bit as without it."""
+    w = workloads.make("b256_v129280")
+    cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+    kept = oracle.budget_select(w.conf, w.draft_len, w.k_max, cost, w.t_base, w.n_bonus)["kept"]
+    target, draft, toks, cu = workload_inputs(w, kept, "stochastic")
+    a = gpu_verify(target, draft, toks, cu, w.k_max, "stochastic", w.tau, logits_dtype(w),
+                   seed=w.seed, step=w.step)
+    b = gpu_verify(target, draft, toks, cu, w.k_max, "stochastic", w.tau, logits_dtype(w),
+                   seed=w.seed, step=w.step, features=True)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    # features at sampled kept positions against the oracle
+    rng = np.random.default_rng(0)
+    for r in rng.choice(w.n, 12, replace=False):
+        for j in range(int(kept[r])):
+            h, m = oracle.draft_features(draft[r * w.k_max + j, : w.vocab], w.tau)
+            assert abs(b["q_entropy"][r, j] - h) <= H_ATOL + H_RTOL * h, (r, j)
+            assert abs(b["q_max"][r, j] - m) <= P_RTOL * m, (r, j)
+    w.drop_cache()
 
 
 # ------------------------------------------------------- shapes and edge cases
@@ -229,7 +255,8 @@ def test_verify_ragged_vocab_and_strides(dtype, V, ld_pad, mode):
         target, draft = bf16_round(target), bf16_round(draft)
     log(f"ragged V={V} ld_pad={ld_pad} {dtype} {mode}")
     g = gpu_verify(target, draft if mode == "stochastic" else None, toks, cu, k, mode, 0.8,
-                   dtype, seed=3, step=11, target_ld=V + ld_pad, draft_ld=V + ld_pad)
+                   dtype, seed=3, step=11, target_ld=V + ld_pad, draft_ld=V + ld_pad,
+                   features=True)
     compare_verify(g, target, draft if mode == "stochastic" else None, toks, cu, k, V, mode, 0.8,
                    3, 11)
 
@@ -242,7 +269,7 @@ def test_verify_no_drafts(mode):
     cu = np.arange(n + 1, dtype=np.int32)
     toks = np.zeros((n, 0), dtype=np.int32)
     draft = np.zeros((0, V), dtype=np.float32) if mode == "stochastic" else None
-    g = gpu_verify(target, draft, toks, cu, 0, mode, 1.0, torch.float32)
+    g = gpu_verify(target, draft, toks, cu, 0, mode, 1.0, torch.float32, features=True)
     compare_verify(g, target, draft, toks, cu, 0, V, mode, 1.0)
     assert (g["accepted"] == 0).all()
 
@@ -269,7 +296,7 @@ def test_verify_faults_and_masks(mode):
     target[cu[5] + 1, 4000] = np.inf               # request 5: +inf logit
     target[cu[7] + 2, :] = -np.inf                 # request 7: target row without mass
     dmode = draft if mode == "stochastic" else None
-    g = gpu_verify(target, dmode, toks, cu, k, mode, 1.0, torch.float32)
+    g = gpu_verify(target, dmode, toks, cu, k, mode, 1.0, torch.float32, features=True)
     compare_verify(g, target, dmode, toks, cu, k, V, mode, 1.0)
     assert g["accepted"][4] >= 0
     assert int(g["dev_error"][0]) != 0
@@ -284,7 +311,7 @@ def test_verify_bad_offsets_never_read_past_target_rows():
     bad[5] = bad[5] + 4       # request 4 runs past the buffer
     for mode in ("stochastic", "greedy"):
         dmode = draft if mode == "stochastic" else None
-        g = gpu_verify(target, dmode, toks, bad, k, mode, 1.0, torch.float32)
+        g = gpu_verify(target, dmode, toks, bad, k, mode, 1.0, torch.float32, features=True)
         compare_verify(g, target, dmode, toks, bad, k, V, mode, 1.0)
         assert int(g["dev_error"][0]) & oracle.DEV_BAD_CU_ROWS
 
@@ -300,8 +327,10 @@ def test_verify_exact_fallback_for_late_large_logit():
     for dtype in (torch.float32, torch.bfloat16):
         t = target if dtype == torch.float32 else bf16_round(target)
         d = draft if dtype == torch.float32 else bf16_round(draft)
-        g = gpu_verify(t, d, toks, cu, k, "stochastic", 1.0, dtype, seed=9)
-        compare_verify(g, t, d, toks, cu, k, V, "stochastic", 1.0, 9)
+        for features in (False, True):
+            g = gpu_verify(t, d, toks, cu, k, "stochastic", 1.0, dtype, seed=9,
+                           features=features)
+            compare_verify(g, t, d, toks, cu, k, V, "stochastic", 1.0, 9)
 
 
 def test_verify_low_temperature_and_ties():
@@ -311,7 +340,8 @@ def test_verify_low_temperature_and_ties():
     target = np.round(target)  # many exact ties
     draft = np.round(draft)
     for tau in (0.05, 3.0):
-        g = gpu_verify(target, draft, toks, cu, k, "stochastic", tau, torch.float32, seed=2)
+        g = gpu_verify(target, draft, toks, cu, k, "stochastic", tau, torch.float32, seed=2,
+                       features=True)
         compare_verify(g, target, draft, toks, cu, k, V, "stochastic", tau, 2)
     g = gpu_verify(target, None, toks, cu, k, "greedy", 1.0, torch.float32)
     compare_verify(g, target, None, toks, cu, k, V, "greedy", 1.0)
@@ -465,14 +495,19 @@ def random_outcomes(rng, n, k):
     q = np.where(rng.uniform(size=(n, k)) < 0.05, 0.0,
                  rng.uniform(1e-4, 1.0, (n, k))).astype(np.float32)
     q[rng.uniform(size=(n, k)) < 0.01] = np.nan
-    return L, cu, q
+    h = rng.uniform(0.0, 12.0, (n, k)).astype(np.float32)   # entropy, bits
+    m = rng.uniform(1e-3, 1.0, (n, k)).astype(np.float32)   # largest probability
+    for a in (h, m):  # not computed (-1) and NaN read as 0
+        a[rng.uniform(size=(n, k)) < 0.02] = -1.0
+        a[rng.uniform(size=(n, k)) < 0.01] = np.nan
+    return L, cu, q, h, m
 
 
 @pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (256, 7), (3000, 15), (100, 64), (5, 0)])
 def test_accept_stats(n, k):
     import adaptive_draft_verification_amd as sv
     rng = np.random.default_rng(n * 7 + k)
-    L, cu, _ = random_outcomes(rng, n, k)
+    L, cu, _, _, _ = random_outcomes(rng, n, k)
     if n > 2:
         L[1] = (cu[2] - cu[1] - 1) + 1  # more accepted than kept: not a verify result
     att = torch.zeros(k, dtype=torch.int64, device="cuda")
@@ -487,28 +522,38 @@ def test_accept_stats(n, k):
     assert tot.cpu().numpy().tolist() == [2 * o["requests"], 2 * o["emitted"]]
 
 
+@pytest.mark.parametrize("features", [True, False])
 @pytest.mark.parametrize("n,k,seed", [(1, 1, 0), (64, 7, 1), (2500, 7, 2), (300, 64, 3),
                                       (50, 3, 4)])
-def test_calibrate_update_and_predict(n, k, seed):
-    """fp32 on the device against the oracle's fp64: theta relative 1e-5
-    (sums of a few thousand sigmoid errors in fp32), the count exact."""
+def test_calibrate_update_and_predict(n, k, seed, features):
+    """fp32 on the device against the oracle's fp64, the count exact.  theta:
+    relative 1e-5, absolute 1e-5 (a gradient component is a fixed-order fp32
+    sum of up to ~2e4 terms |err * x| <= 12, divided by the count: its
+    rounding stays below ~4e-6 per unit of lr).  conf: absolute 2e-6 (log2 of
+    the fp32 probability to 1 ulp, about 1e-6 of the logit for |x_1| <= 16,
+    times the sigmoid's slope <= 1/4, plus the fp32 sigmoid)."""
     import adaptive_draft_verification_amd as sv
     rng = np.random.default_rng(seed)
-    L, cu, q = random_outcomes(rng, n, k)
-    theta = rng.normal(0, 1, k + 1).astype(np.float32)
+    L, cu, q, h, m = random_outcomes(rng, n, k)
+    if not features:
+        h = m = None
+    dv = lambda a: None if a is None else to_dev(a)
+    theta = rng.normal(0, 0.5, k + 3).astype(np.float32)
     th = to_dev(theta)
     cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
-    sv.sv_calibrate_update(th, to_dev(q), to_dev(L), to_dev(cu), 0.5, cnt)
+    sv.sv_calibrate_update(th, to_dev(q), to_dev(L), to_dev(cu), 0.5, cnt, q_entropy=dv(h),
+                           q_max=dv(m))
     torch.cuda.synchronize()
-    want, count = oracle.calibrate_update(theta.astype(np.float64), q, L, cu, k, 0.5)
+    want, count = oracle.calibrate_update(theta.astype(np.float64), q, L, cu, k, 0.5, h, m)
     assert int(cnt.cpu()[0]) == count
-    np.testing.assert_allclose(th.cpu().numpy(), want, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(th.cpu().numpy(), want, rtol=1e-5, atol=1e-5)
     conf = torch.empty(n, k, dtype=torch.float32, device="cuda")
-    sv.sv_calibrate_predict(th, to_dev(q), conf)
+    sv.sv_calibrate_predict(th, to_dev(q), conf, q_entropy=dv(h), q_max=dv(m))
     torch.cuda.synchronize()
-    np.testing.assert_allclose(conf.cpu().numpy(),
-                               oracle.calibrate_predict(th.cpu().numpy().astype(np.float64), q, k),
-                               rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(
+        conf.cpu().numpy(),
+        oracle.calibrate_predict(th.cpu().numpy().astype(np.float64), q, k, h, m),
+        rtol=2e-6, atol=2e-6)
 
 
 def test_calibration_from_a_verify_step():
@@ -527,21 +572,28 @@ def test_calibration_from_a_verify_step():
     b = sv.budget_select(to_dev(w.conf), to_dev(w.draft_len), to_dev(cost), w.t_base, w.n_bonus)
     p = sv.pack_varlen(b["kept"], to_dev(w.last_token), to_dev(toks))
     v = sv.verify(to_dev(target, dt), to_dev(draft, dt), to_dev(toks), p["cu_rows"],
-                  sv.SV_STOCHASTIC, w.tau, w.seed, w.step)
+                  sv.SV_STOCHASTIC, w.tau, w.seed, w.step, features=True)
     k = w.k_max
     att = torch.zeros(k, dtype=torch.int64, device="cuda")
     acc = torch.zeros(k, dtype=torch.int64, device="cuda")
     tot = torch.zeros(2, dtype=torch.int64, device="cuda")
     sv.sv_accept_stats(v["accepted"], p["cu_rows"], att, acc, tot)
-    theta = torch.zeros(k + 1, dtype=torch.float32, device="cuda")
-    sv.sv_calibrate_update(theta, v["q_draft"], v["accepted"], p["cu_rows"], 1.0)
+    theta = torch.zeros(k + 3, dtype=torch.float32, device="cuda")
+    sv.sv_calibrate_update(theta, v["q_draft"], v["accepted"], p["cu_rows"], 1.0,
+                           q_entropy=v["q_entropy"], q_max=v["q_max"])
     torch.cuda.synchronize()
     L = v["accepted"].cpu().numpy()
     cu = p["cu_rows"].cpu().numpy()
     q = v["q_draft"].cpu().numpy()
+    h, m = v["q_entropy"].cpu().numpy(), v["q_max"].cpu().numpy()
     o = oracle.accept_stats(L, cu, k)
     np.testing.assert_array_equal(att.cpu().numpy(), o["attempted"])
     np.testing.assert_array_equal(acc.cpu().numpy(), o["accepted_at"])
     assert tot.cpu().numpy().tolist() == [o["requests"], o["emitted"]] and o["requests"] == w.n
-    want, _ = oracle.calibrate_update(np.zeros(k + 1), q, L, cu, k, 1.0)
-    np.testing.assert_allclose(theta.cpu().numpy(), want, rtol=1e-5, atol=1e-6)
+    want, _ = oracle.calibrate_update(np.zeros(k + 3), q, L, cu, k, 1.0, h, m)
+    np.testing.assert_allclose(theta.cpu().numpy(), want, rtol=1e-5, atol=1e-5)
+    # the features themselves: the oracle's, at the kept positions
+    for r in range(0, w.n, 7):
+        for j in range(int(o_b["kept"][r])):
+            eh, em = oracle.draft_features(draft[r * k + j, : w.vocab], w.tau)
+            assert abs(h[r, j] - eh) <= H_ATOL + H_RTOL * eh and abs(m[r, j] - em) <= P_RTOL * em
