@@ -28,6 +28,10 @@ Parity pin status (what the oracle is checked against, in tests/):
 * budget_select — pinned by exhaustive exact-rational search over every
   per-request allocation on small cases, by the truncated-k table read as a
   cost model, and by prefix-closure invariants.
+* budget_allocate (a budget sized elsewhere, slots from the current
+  confidences) — pinned by exhaustive exact-rational search (the kept slots
+  carry the largest survival total of any prefix allocation of B slots), by
+  equality with budget_select at its own B, and by the edge readings.
 * uniform_k_select — pinned by the FOS truncated-k table (tokens per computed
   position is its goodput for one request whose step cost grows with the
   positions computed), by exact-rational search, by equality with the budget
@@ -67,6 +71,7 @@ from .budget import (
     expected_tokens,
     budget_score,
     budget_select,
+    budget_allocate,
     DEV_BAD_DRAFT_LEN,
     DEV_BAD_COST,
 )
@@ -92,7 +97,7 @@ from .verify import (
 __all__ = [
     "philox4x32_10", "uniforms", "PHILOX_ROUNDS",
     "clamp_confidence", "survival", "cost_table_prepare", "rank_slots",
-    "fixed_point", "expected_tokens", "budget_score", "budget_select", "uniform_k_select",
+    "fixed_point", "expected_tokens", "budget_score", "budget_select", "budget_allocate", "uniform_k_select",
     "accept_stats", "calibrate_update", "calibrate_predict", "draft_features",
     "pack_varlen", "row_probs", "accept", "residual_weights", "inverse_cdf",
     "row_is_faulty", "verify_request", "verify", "GREEDY", "STOCHASTIC",

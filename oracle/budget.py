@@ -188,3 +188,25 @@ def budget_select(conf, draft_len, k_max, cost, t_base, n_bonus):
         kept[r] += 1
     return dict(kept=kept, budget=best_b, survival=s, dev_error=err,
                 order=order, scores=scores, lens=lens)
+
+
+def budget_allocate(conf, draft_len, k_max, budget):
+    """Kept draft counts for a budget B sized elsewhere.
+
+    agentlens page, section "DSpark 신뢰도 스케줄링 메커니즘", item Execution
+    Pipeline: B is sized ahead of time from the previous step's confidences,
+    and only the allocation of slots to requests runs with the current ones;
+    the allocation is the same Global Top-B Selection (the B best slots of
+    the global ranking, a contiguous prefix per request).  Reading: a B above
+    the current number of slots keeps every slot, a negative B keeps none.
+
+    Returns dict(kept, budget_used, survival, dev_error).
+    """
+    n = len(draft_len)
+    s, lens, err = survival(conf, draft_len, k_max)
+    order = rank_slots(s, lens)
+    used = min(max(int(budget), 0), len(order))
+    kept = np.zeros(n, dtype=np.int32)
+    for r, _j in order[:used]:
+        kept[r] += 1
+    return dict(kept=kept, budget_used=used, survival=s, dev_error=err)
