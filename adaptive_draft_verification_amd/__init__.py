@@ -27,7 +27,8 @@ SV_DEV_BAD_DRAFT_LEN, SV_DEV_BAD_COST, SV_DEV_BAD_KEPT = 8, 16, 32
 SV_MAX_BUDGET_SLOTS, SV_MAX_DRAFT, SV_MAX_VOCAB = 8192, 64, 1048576
 
 EXPORTED = ["sv_status_str", "sv_budget_workspace_bytes", "sv_verify_workspace_bytes",
-            "sv_cost_table_prepare", "sv_budget_select", "sv_uniform_k_select", "sv_pack_varlen",
+            "sv_cost_table_prepare", "sv_budget_select", "sv_budget_allocate",
+            "sv_uniform_k_select", "sv_pack_varlen",
             "sv_verify",
             "sv_verify_stages", "sv_accept_stats", "sv_calibrate_update", "sv_calibrate_predict",
             "sv_philox_uniforms"]
@@ -54,6 +55,7 @@ def _load():
         "sv_cost_table_prepare": (ctypes.c_int, [vp, i32, i32, vp, i32]),
         "sv_budget_select": (ctypes.c_int, [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp,
                                             vp, sz, vp]),
+        "sv_budget_allocate": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "sv_uniform_k_select": (ctypes.c_int, [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp,
                                                vp, vp]),
         "sv_pack_varlen": (ctypes.c_int, [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]),
@@ -151,6 +153,30 @@ def sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survi
                                  _ptr(survival), _ptr(dev_error), _ptr(ws), 0 if ws is None else ws.numel(),
                                  _stream(stream)),
            "sv_budget_select")
+
+
+def sv_budget_allocate(conf, draft_len, budget_in, kept, budget_used=None, survival=None,
+                       dev_error=None, stream=None, ws=None):
+    """conf [n, k_max] f32, draft_len [n] i32, budget_in [1] i32 (device) -> kept [n] i32.
+
+    ws: device uint8 tensor of at least sv_budget_workspace_bytes(n, k_max) bytes."""
+    _dev(conf, torch.float32, "conf", 2)
+    _dev(draft_len, torch.int32, "draft_len", 1)
+    _dev(budget_in, torch.int32, "budget_in", 1)
+    _dev(kept, torch.int32, "kept", 1)
+    _dev(budget_used, torch.int32, "budget_used", 1)
+    _dev(survival, torch.float32, "survival", 2)
+    _dev(dev_error, torch.int32, "dev_error", 1)
+    _dev(ws, torch.uint8, "ws", 1)
+    n, k_max = conf.shape
+    if draft_len.numel() != n or kept.numel() != n or budget_in.numel() < 1:
+        raise ValueError("draft_len, kept must have n entries and budget_in one")
+    if survival is not None and tuple(survival.shape) != (n, k_max):
+        raise ValueError("survival must be [n, k_max]")
+    _check(_lib.sv_budget_allocate(_ptr(conf), _ptr(draft_len), n, k_max, _ptr(budget_in),
+                                   _ptr(kept), _ptr(budget_used), _ptr(survival), _ptr(dev_error),
+                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "sv_budget_allocate")
 
 
 def sv_uniform_k_select(conf, draft_len, cost, t_base, n_bonus, kept, k_out, scores=None,
@@ -341,6 +367,21 @@ def budget_select(conf, draft_len, cost, t_base, n_bonus, stream=None):
     sv_budget_select(conf, draft_len, cost, t_base, n_bonus, kept, budget, survival, err, stream,
                      ws=ws)
     return dict(kept=kept, budget=budget, survival=survival, dev_error=err)
+
+
+def budget_allocate(conf, draft_len, budget_in, stream=None, ws=None):
+    dev = conf.device
+    n, k_max = conf.shape
+    out = dict(kept=torch.empty(n, dtype=torch.int32, device=dev),
+               budget_used=torch.empty(1, dtype=torch.int32, device=dev),
+               survival=torch.empty(n, k_max, dtype=torch.float32, device=dev),
+               dev_error=torch.zeros(1, dtype=torch.int32, device=dev))
+    if ws is None:
+        ws = torch.empty(max(1, sv_budget_workspace_bytes(n, k_max)), dtype=torch.uint8,
+                         device=dev)
+    sv_budget_allocate(conf, draft_len, budget_in, out["kept"], out["budget_used"],
+                       out["survival"], out["dev_error"], stream, ws=ws)
+    return out
 
 
 def uniform_k_select(conf, draft_len, cost, t_base, n_bonus, stream=None):

@@ -86,6 +86,24 @@ sv_status sv_budget_select(const float* conf, const int32_t* draft_len, int32_t 
                                       budget, survival, dev_error, ws, as_stream(stream)));
 }
 
+sv_status sv_budget_allocate(const float* conf, const int32_t* draft_len, int32_t n_req,
+                             int32_t k_max, const int32_t* budget_in, int32_t* kept,
+                             int32_t* budget_used, float* survival, int32_t* dev_error, void* ws,
+                             size_t ws_bytes, void* stream) {
+    if (n_req < 0 || k_max < 0) return SV_ERR_SHAPE;
+    if (budget_in == nullptr) return SV_ERR_NULL;
+    if (n_req > 0 && (draft_len == nullptr || kept == nullptr)) return SV_ERR_NULL;
+    if (n_req > 0 && k_max > 0 && conf == nullptr) return SV_ERR_NULL;
+    if (n_req > SV_MAX_BUDGET_SLOTS || k_max > SV_MAX_DRAFT ||
+        (int64_t)n_req * k_max > SV_MAX_BUDGET_SLOTS)
+        return SV_ERR_SHAPE;
+    const size_t need = sv::budget_workspace_bytes(n_req, k_max);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return SV_ERR_WORKSPACE;
+    return launched(sv::launch_allocate(conf, draft_len, n_req, k_max, budget_in, kept,
+                                        budget_used, survival, dev_error, ws,
+                                        as_stream(stream)));
+}
+
 sv_status sv_uniform_k_select(const float* conf, const int32_t* draft_len, int32_t n_req,
                               int32_t k_max, const float* cost, int32_t cost_len, int32_t t_base,
                               int32_t n_bonus, int32_t* kept, int32_t* k_out, double* scores,

@@ -201,6 +201,28 @@ struct BetterOp {
     }
 };
 
+// kept[r] = #{j : rank(r, j) < B}.  rk[q] holds the rank of slot
+// tid + 1024 q (slots past draft_len rank at `total` or later, never before
+// B <= total).  Every thread of the workgroup calls this (one barrier).
+__device__ __forceinline__ void write_kept(const int32_t* rk, int per, int B, int n_req,
+                                           int k_max, uint8_t* in_budget,
+                                           int32_t* __restrict__ kept) {
+    const int tid = threadIdx.x;
+    const int n_slots = n_req * k_max;
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        if (q >= per) break;  // uniform
+        const int x = tid + q * kThreads;
+        if (x < n_slots) in_budget[x] = rk[q] < B ? 1 : 0;
+    }
+    __syncthreads();
+    for (int r = tid; r < n_req; r += kThreads) {
+        int k_in = 0;
+        for (int j = 0; j < k_max; ++j) k_in += in_budget[r * k_max + j];
+        kept[r] = k_in;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void finish_kernel(
     int n_req, int k_max, const float* __restrict__ cost, int t_base, int n_bonus,
     int32_t* __restrict__ kept, int32_t* __restrict__ budget, int32_t* dev_error, void* ws) {
@@ -291,25 +313,39 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     }
     __syncthreads();
     const int B = best_b_s;
-
-    // kept counts: a request's slots ranked before B (slots past draft_len
-    // rank at `total` or later, never before B)
-#pragma unroll
-    for (int q = 0; q < kPerThread; ++q) {
-        if (q >= per) break;  // uniform
-        const int x = tid + q * kThreads;
-        if (x < n_slots) in_budget[x] = rk[q] < B ? 1 : 0;
-    }
-    __syncthreads();
-    for (int r = tid; r < n_req; r += kThreads) {
-        int k_in = 0;
-        for (int j = 0; j < k_max; ++j) k_in += in_budget[r * k_max + j];
-        kept[r] = k_in;
-    }
+    write_kept(rk, per, B, n_req, k_max, in_budget, kept);
     if (tid == 0) {
         budget[0] = B;
         raise_error(dev_error, err_s);
     }
+}
+
+// Allocation of a budget sized elsewhere (agentlens page, section "DSpark
+// 신뢰도 스케줄링 메커니즘", item Execution Pipeline: B comes from the
+// previous step's confidences, the slots from the current ones): the first
+// min(max(B, 0), total) slots of the rank kernel's order.  One workgroup.
+__global__ __launch_bounds__(kThreads) void allocate_kernel(int n_req, int k_max,
+                                                            const int32_t* __restrict__ budget_in,
+                                                            int32_t* __restrict__ kept,
+                                                            int32_t* budget_used, void* ws) {
+    __shared__ uint8_t in_budget[SV_MAX_BUDGET_SLOTS];
+    const int tid = threadIdx.x;
+    const int n_slots = n_req * k_max;
+    const BudgetWs w = budget_ws(ws, n_slots);
+    const int per = (n_slots + kThreads - 1) / kThreads;
+    int32_t rk[kPerThread];
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        rk[q] = 0;
+        if (q >= per) continue;  // uniform
+        const int x = tid + q * kThreads;
+        if (x < n_slots) rk[q] = w.rank[x];
+    }
+    const int total = n_slots > 0 ? w.total[0] : 0;
+    const int b_in = budget_in[0];
+    const int B = b_in < 0 ? 0 : (b_in > total ? total : b_in);
+    write_kept(rk, per, B, n_req, k_max, in_budget, kept);
+    if (tid == 0 && budget_used != nullptr) budget_used[0] = B;
 }
 
 // One draft length for the whole batch ("Hardware-Aware Dynamic Speculative
@@ -423,20 +459,36 @@ size_t budget_workspace_bytes(int n_req, int k_max) {
     return kHeaderBytes + (size_t)n_req * (size_t)k_max * (sizeof(int32_t) + sizeof(float));
 }
 
+hipError_t launch_rank(const float* conf, const int32_t* draft_len, int n_req, int k_max,
+                       float* survival, int32_t* dev_error, void* ws, hipStream_t stream) {
+    if (n_req == 0) return hipSuccess;
+    const int n_slots = n_req * k_max;
+    const unsigned blocks = (unsigned)(n_slots > 0 ? (n_slots + kQueries - 1) / kQueries : 1);
+    hipLaunchKernelGGL(rank_kernel, dim3(blocks), dim3(kThreads), 0, stream, conf, draft_len,
+                       n_req, k_max, survival, dev_error, ws);
+    return hipGetLastError();
+}
+
 hipError_t launch_budget(const float* conf, const int32_t* draft_len, int n_req, int k_max,
                          const float* cost, int t_base, int n_bonus, int32_t* kept,
                          int32_t* budget, float* survival, int32_t* dev_error, void* ws,
                          hipStream_t stream) {
-    const int n_slots = n_req * k_max;
-    if (n_req > 0) {
-        const unsigned blocks = (unsigned)(n_slots > 0 ? (n_slots + kQueries - 1) / kQueries : 1);
-        hipLaunchKernelGGL(rank_kernel, dim3(blocks), dim3(kThreads), 0, stream, conf, draft_len,
-                           n_req, k_max, survival, dev_error, ws);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    const hipError_t e = launch_rank(conf, draft_len, n_req, k_max, survival, dev_error, ws,
+                                     stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kThreads), 0, stream, n_req, k_max, cost,
                        t_base, n_bonus, kept, budget, dev_error, ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_allocate(const float* conf, const int32_t* draft_len, int n_req, int k_max,
+                           const int32_t* budget_in, int32_t* kept, int32_t* budget_used,
+                           float* survival, int32_t* dev_error, void* ws, hipStream_t stream) {
+    const hipError_t e = launch_rank(conf, draft_len, n_req, k_max, survival, dev_error, ws,
+                                     stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(allocate_kernel, dim3(1), dim3(kThreads), 0, stream, n_req, k_max,
+                       budget_in, kept, budget_used, ws);
     return hipGetLastError();
 }
 

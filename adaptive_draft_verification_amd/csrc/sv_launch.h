@@ -14,6 +14,9 @@ hipError_t launch_budget(const float* conf, const int32_t* draft_len, int n_req,
                          const float* cost, int t_base, int n_bonus, int32_t* kept,
                          int32_t* budget, float* survival, int32_t* dev_error, void* ws,
                          hipStream_t stream);
+hipError_t launch_allocate(const float* conf, const int32_t* draft_len, int n_req, int k_max,
+                           const int32_t* budget_in, int32_t* kept, int32_t* budget_used,
+                           float* survival, int32_t* dev_error, void* ws, hipStream_t stream);
 size_t budget_workspace_bytes(int n_req, int k_max);
 
 hipError_t launch_uniform_k(const float* conf, const int32_t* draft_len, int n_req, int k_max,

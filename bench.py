@@ -23,7 +23,8 @@ rows each draw reads again) are reported beside it.  A second leg verifies
 every draft (full K: 2048 target + 1792 draft rows) for the bandwidth figure
 at the largest size.  Two smaller legs time pass 1 with the draft-row
 features (entropy, largest probability) accumulated as well, and the one-K-
-per-batch selection (sv_uniform_k_select).  The CPU oracle runs whole steps of
+per-batch selection (sv_uniform_k_select), and the allocation of a budget
+sized one step ahead (sv_budget_allocate).  The CPU oracle runs whole steps of
 the same workload on the host for the cpu_baseline figure.
 
 Prints one JSON line.
@@ -386,6 +387,19 @@ def main():
     uniform_k = {"us": round(e0.elapsed_time(e1) / args.steps * 1e3, 2), "k": int(uk_k.item()),
                  "drafts_verified": int(uk_kept.sum().item())}
 
+    # ----------------------------------------- stale-confidence budget leg
+    # the pipeline that sizes B one step ahead: the step itself only allocates
+    # the slots of a B already in device memory (here the budget selected above)
+    al_kept = torch.empty(n, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        sv.sv_budget_allocate(conf_d, dl_d, budget, al_kept, None, None, err, ws=bws)
+    e0.record(stream)
+    for _ in range(args.steps):
+        sv.sv_budget_allocate(conf_d, dl_d, budget, al_kept, None, None, err, ws=bws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    budget_allocate_us = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
+
     # ------------------------------------------------------------ CPU oracle leg
     cpu = None
     if not args.no_cpu_baseline:
@@ -435,6 +449,7 @@ def main():
                      "bytes_per_launch": int(pass1_bytes),
                      "launch_us": round(roof_ms * 1e3, 2)},
         "budget_select_us": round(float(np.mean(stage_ms[:, 0])) * 1e3, 2),
+        "budget_allocate_us": budget_allocate_us,
         "pack_us": round(float(np.mean(stage_ms[:, 1])) * 1e3, 2),
         "verify_pass1_us": round(pass1_ms * 1e3, 2),
         "verify_pass2_us": round(pass2_ms * 1e3, 2),

@@ -131,7 +131,7 @@ sv_status sv_cost_table_prepare(const float* raw, int32_t raw_len, int32_t granu
  *            that size is 0 (n_req = 0).  Calls that overlap in time must
  *            not share a workspace.
  * Launch: two kernels on `stream`.  The first ranks every slot: one
- * 1024-thread workgroup per 64 slots counts, for each of its slots, the
+ * 1024-thread workgroup per 16 slots counts, for each of its slots, the
  * keys of the whole batch ordered before it (the keys staged in LDS).  The
  * second, one workgroup of 1024 threads, scans the rank-ordered survivals
  * and picks B.
@@ -144,6 +144,34 @@ sv_status sv_budget_select(const float* conf, const int32_t* draft_len, int32_t 
                            int32_t k_max, const float* cost, int32_t cost_len, int32_t t_base,
                            int32_t n_bonus, int32_t* kept, int32_t* budget, float* survival,
                            int32_t* dev_error, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sv_budget_allocate — the slots of a budget B sized elsewhere.
+ *
+ * agentlens page, section "DSpark 신뢰도 스케줄링 메커니즘", item Execution
+ * Pipeline: the budget is sized from the previous step's (double-buffered)
+ * confidences, ahead of the step, and only the allocation of slots to
+ * requests runs with the current step's.  Here B is read on the device
+ * (budget_in, e.g. the `budget` sv_budget_select wrote for the previous
+ * step's confidences, copied to the host asynchronously to size the batch)
+ * and the current confidences are ranked exactly as in sv_budget_select
+ * steps 1-2; kept[r] = number of request r's slots among the first
+ * min(max(B, 0), total slots).
+ *
+ * conf, draft_len, survival, ws: as sv_budget_select (same workspace size).
+ * budget_in:   [1] int32 device, B (a B above the current slot count keeps
+ *              every slot; B <= 0 keeps none).
+ * kept:        [n_req] int32 out.
+ * budget_used: [1] int32 out, the B applied after clamping, or NULL.
+ * Launch: the rank kernel of sv_budget_select, then one 1024-thread
+ * workgroup that counts each request's slots ranked below B.
+ * Errors: SV_ERR_NULL (budget_in always; conf, draft_len, kept when there
+ * are requests); SV_ERR_SHAPE as sv_budget_select; SV_ERR_WORKSPACE.
+ */
+sv_status sv_budget_allocate(const float* conf, const int32_t* draft_len, int32_t n_req,
+                             int32_t k_max, const int32_t* budget_in, int32_t* kept,
+                             int32_t* budget_used, float* survival, int32_t* dev_error, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /*
  * sv_uniform_k_select — one draft length K for the whole batch, by goodput.

@@ -78,6 +78,21 @@ def check_budget(conf, draft_len, k_max, cost, t_base, n_bonus):
     return o
 
 
+def check_allocate(conf, draft_len, k_max, budget):
+    """Allocation of a given budget: kept counts, the clamped B, survival bits."""
+    conf = np.asarray(conf, np.float32).reshape(len(draft_len), k_max)
+    g = sv.budget_allocate(to_dev(conf), to_dev(np.asarray(draft_len, np.int32)),
+                           to_dev(np.array([budget], np.int32)))
+    torch.cuda.synchronize()
+    o = oracle.budget_allocate(conf, draft_len, k_max, budget)
+    np.testing.assert_array_equal(g["kept"].cpu().numpy(), o["kept"])
+    assert int(g["budget_used"].cpu()[0]) == o["budget_used"]
+    np.testing.assert_array_equal(g["survival"].cpu().numpy().view(np.uint32),
+                                  o["survival"].view(np.uint32))
+    assert int(g["dev_error"].cpu()[0]) == o["dev_error"]
+    return o
+
+
 def check_uniform_k(conf, draft_len, k_max, cost, t_base, n_bonus):
     """Uniform draft length: K*, kept counts and every K's fp64 score exact."""
     conf = np.asarray(conf, np.float32).reshape(len(draft_len), k_max)

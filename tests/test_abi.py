@@ -92,6 +92,26 @@ def budget(**kw):
     return sv._lib.sv_budget_select(*args.values())
 
 
+def allocate(**kw):
+    args = dict(conf=FAKE, draft_len=FAKE, n_req=4, k_max=3, budget_in=FAKE, kept=FAKE,
+                budget_used=None, survival=None, dev_error=None, ws=FAKE,
+                ws_bytes=sv.sv_budget_workspace_bytes(4, 3), stream=None)
+    args.update(kw)
+    return sv._lib.sv_budget_allocate(*args.values())
+
+
+def test_budget_allocate_host_validation():
+    assert allocate(n_req=-1) == sv.SV_ERR_SHAPE
+    assert allocate(k_max=-1) == sv.SV_ERR_SHAPE
+    assert allocate(n_req=2048, k_max=5) == sv.SV_ERR_SHAPE   # > 8192 slots
+    assert allocate(n_req=8193, k_max=0) == sv.SV_ERR_SHAPE   # > 8192 requests
+    assert allocate(n_req=1, k_max=65) == sv.SV_ERR_SHAPE     # > 64 drafts
+    for key in ("budget_in", "conf", "draft_len", "kept"):
+        assert allocate(**{key: None}) == sv.SV_ERR_NULL, key
+    assert allocate(ws=None) == sv.SV_ERR_WORKSPACE
+    assert allocate(ws_bytes=sv.sv_budget_workspace_bytes(4, 3) - 1) == sv.SV_ERR_WORKSPACE
+
+
 def test_budget_select_host_validation():
     assert budget(cost_len=16) == sv.SV_ERR_SHAPE          # needs t_base + n*k + 1
     assert budget(n_req=-1) == sv.SV_ERR_SHAPE

@@ -14,7 +14,8 @@ import torch
 import oracle
 import workloads
 
-from parity import (H_ATOL, H_RTOL, P_RTOL, check_budget, check_pack, check_uniform_k,
+from parity import (H_ATOL, H_RTOL, P_RTOL, check_allocate, check_budget, check_pack,
+                    check_uniform_k,
                     compare_verify, gpu_verify, logits_dtype, to_dev, workload_inputs)
 
 pytestmark = pytest.mark.gpu
@@ -95,6 +96,136 @@ def test_budget_denormal_survivals():
     dl = np.full(4, 6, dtype=np.int32)
     cost = np.ones(4 + 24 + 1, dtype=np.float32)
     check_budget(conf, dl, 6, cost, 4, 4)
+
+
+# ------------------------------------------- a budget sized from stale confidences
+
+@pytest.mark.parametrize("seed", range(24))
+def test_budget_allocate_random(seed):
+    rng = np.random.default_rng(700 + seed)
+    n = int(rng.integers(1, 300))
+    k = int(rng.integers(1, min(16, 8192 // n) + 1))
+    conf, dl, _cost, _t, _nb = workloads.random_budget_case(rng, n, k, ties=seed % 2 == 0,
+                                                            zeros=seed % 3 == 0)
+    if seed % 7 == 0:
+        dl[0] = k + 2
+        conf[-1, 0] = np.nan
+    total = int(np.clip(dl, 0, k).sum())
+    for B in (-3, 0, 1, int(rng.integers(0, total + 1)), total, total + 5):
+        check_allocate(conf, dl, k, B)
+
+
+@pytest.mark.parametrize("n,k", [(8192, 1), (1024, 8), (128, 64), (1, 1), (3, 0), (0, 4)])
+def test_budget_allocate_edges(n, k):
+    rng = np.random.default_rng(n * 3 + k)
+    conf = rng.uniform(0.3, 1.0, (n, k)).astype(np.float32)
+    dl = rng.integers(0, k + 1, n).astype(np.int32)
+    for B in (0, n * k // 3, n * k):
+        check_allocate(conf, dl, k, B)
+
+
+def test_stale_budget_pipeline():
+    """The agentlens Execution Pipeline on one stream: step t's budget is sized
+    from step t-1's confidences (double-buffered on the device) and reaches the
+    host through an asynchronous copy into pinned memory; the slots come from
+    step t's confidences on the device; pack and verify follow.  Each stage
+    against the oracle fed the same inputs."""
+    import adaptive_draft_verification_amd as sv
+    w = workloads.make("b64_v128256")
+    n, k = w.n, w.k_max
+    cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+    rng = np.random.default_rng(3)
+    steps = 4
+    confs = [w.conf] + [(rng.beta(8, 2, (n, 1)) ** np.arange(1, k + 1)).astype(np.float32)
+                        for _ in range(steps - 1)]
+    conf_buf = [torch.empty(n, k, dtype=torch.float32, device="cuda") for _ in range(2)]
+    dl, cost_d = to_dev(w.draft_len), to_dev(cost)
+    toks = w.draft_tokens("stochastic")
+    budget_dev = torch.empty(1, dtype=torch.int32, device="cuda")
+    kept_sel = torch.empty(n, dtype=torch.int32, device="cuda")
+    b_host = torch.empty(1, dtype=torch.int32).pin_memory()
+    copied = torch.cuda.Event()
+    ws = torch.empty(sv.sv_budget_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    draft_full = workloads.assemble_draft(w, w.draft_len)
+    for t in range(steps):
+        cur = conf_buf[t % 2]
+        cur.copy_(torch.from_numpy(confs[t]))            # the drafter's estimates of step t
+        prev = conf_buf[(t - 1) % 2] if t > 0 else cur  # step 0 has no previous step
+        prev_np = confs[t - 1] if t > 0 else confs[0]
+        sv.sv_budget_select(prev, dl, cost_d, w.t_base, w.n_bonus, kept_sel, budget_dev, ws=ws)
+        b_host.copy_(budget_dev, non_blocking=True)
+        copied.record()
+        copied.synchronize()                             # the scheduler sizes the batch
+        B = int(b_host[0])
+        assert B == oracle.budget_select(prev_np, w.draft_len, k, cost, w.t_base,
+                                         w.n_bonus)["budget"]
+        a = sv.budget_allocate(cur, dl, budget_dev, ws=ws)
+        p = sv.pack_varlen(a["kept"], to_dev(w.last_token), to_dev(toks))
+        o_a = oracle.budget_allocate(confs[t], w.draft_len, k, B)
+        np.testing.assert_array_equal(a["kept"].cpu().numpy(), o_a["kept"])
+        kept = o_a["kept"]
+        o_p = oracle.pack_varlen(kept, w.last_token, toks, k)
+        np.testing.assert_array_equal(p["cu_rows"].cpu().numpy(), o_p["cu_rows"])
+        target = workloads.assemble_target(w, o_p["cu_rows"], kept)
+        v = sv.verify(to_dev(target, logits_dtype(w)), to_dev(draft_full, logits_dtype(w)),
+                      to_dev(toks), p["cu_rows"], sv.SV_STOCHASTIC, w.tau, w.seed, t)
+        torch.cuda.synchronize()
+        g = {key: val.cpu().numpy() for key, val in v.items()}
+        compare_verify(g, target, draft_full, toks, o_p["cu_rows"], k, w.vocab, "stochastic",
+                       w.tau, w.seed, t)
+        log(f"step {t}: B={B} rows={int(o_p['cu_rows'][-1])}")
+    w.drop_cache()
+
+
+def test_allocate_graph_replay_follows_the_budget_in_memory():
+    """allocate -> pack captured once; replays read whatever B and confidences
+    sit in their device buffers (written by kernels between replays)."""
+    import adaptive_draft_verification_amd as sv
+    rng = np.random.default_rng(12)
+    n, k = 200, 7
+    conf_np = [(rng.beta(8, 2, (n, 1)) ** np.arange(1, k + 1)).astype(np.float32)
+               for _ in range(3)]
+    dl_np = rng.integers(0, k + 1, n).astype(np.int32)
+    conf, dl = torch.empty(n, k, dtype=torch.float32, device="cuda"), to_dev(dl_np)
+    b_in = torch.zeros(1, dtype=torch.int32, device="cuda")
+    last, toks = to_dev(rng.integers(0, 999, n).astype(np.int32)), \
+        to_dev(rng.integers(0, 999, (n, k)).astype(np.int32))
+    ws = torch.empty(sv.sv_budget_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    kept = torch.empty(n, dtype=torch.int32, device="cuda")
+    used = torch.empty(1, dtype=torch.int32, device="cuda")
+    cap = n * (k + 1)
+    cu = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    rr, rp, pt = (torch.empty(cap, dtype=torch.int32, device="cuda") for _ in range(3))
+
+    def body():
+        sv.sv_budget_allocate(conf, dl, b_in, kept, used, ws=ws)
+        sv.sv_pack_varlen(kept, last, toks, cu, rr, rp, pt)
+
+    conf.copy_(torch.from_numpy(conf_np[0]))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    total = int(np.clip(dl_np, 0, k).sum())
+    for i, B in enumerate([0, 17, total // 2, total + 3, 5]):
+        c = conf_np[i % 3]
+        conf.copy_(torch.from_numpy(c))
+        b_in.fill_(B)
+        g.replay()
+        torch.cuda.synchronize()
+        o = oracle.budget_allocate(c, dl_np, k, B)
+        np.testing.assert_array_equal(kept.cpu().numpy(), o["kept"], err_msg=f"replay {i}")
+        assert int(used.cpu()[0]) == o["budget_used"]
+        o_p = oracle.pack_varlen(o["kept"], last.cpu().numpy(), toks.cpu().numpy(), k)
+        np.testing.assert_array_equal(cu.cpu().numpy(), o_p["cu_rows"], err_msg=f"replay {i}")
+        body()  # eager work between replays
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(kept.cpu().numpy(), o["kept"])
 
 
 # ------------------------------------------------------- uniform draft length
