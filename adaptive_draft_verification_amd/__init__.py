@@ -28,6 +28,7 @@ SV_MAX_BUDGET_SLOTS, SV_MAX_DRAFT, SV_MAX_VOCAB = 8192, 64, 1048576
 
 EXPORTED = ["sv_status_str", "sv_budget_workspace_bytes", "sv_verify_workspace_bytes",
             "sv_cost_table_prepare", "sv_budget_select", "sv_budget_allocate",
+            "sv_budget_select_pack", "sv_budget_allocate_pack",
             "sv_uniform_k_select", "sv_pack_varlen",
             "sv_verify",
             "sv_verify_stages", "sv_accept_stats", "sv_calibrate_update", "sv_calibrate_predict",
@@ -56,6 +57,10 @@ def _load():
         "sv_budget_select": (ctypes.c_int, [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp,
                                             vp, sz, vp]),
         "sv_budget_allocate": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "sv_budget_select_pack": (ctypes.c_int, [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp,
+                                                 vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "sv_budget_allocate_pack": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                   vp, vp, vp, vp, vp, sz, vp]),
         "sv_uniform_k_select": (ctypes.c_int, [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp,
                                                vp, vp]),
         "sv_pack_varlen": (ctypes.c_int, [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]),
@@ -177,6 +182,65 @@ def sv_budget_allocate(conf, draft_len, budget_in, kept, budget_used=None, survi
                                    _ptr(kept), _ptr(budget_used), _ptr(survival), _ptr(dev_error),
                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "sv_budget_allocate")
+
+
+def _pack_outputs(n, k_max, last_token, draft_tokens, cu_rows, row_req, row_pos, packed_tokens):
+    for name, t in (("last_token", last_token), ("cu_rows", cu_rows), ("row_req", row_req),
+                    ("row_pos", row_pos), ("packed_tokens", packed_tokens)):
+        _dev(t, torch.int32, name, 1)
+    _dev(draft_tokens, torch.int32, "draft_tokens", 2)
+    cap = n * (k_max + 1)
+    if tuple(draft_tokens.shape) != (n, k_max) or last_token.numel() != n \
+            or cu_rows.numel() != n + 1:
+        raise ValueError("draft_tokens [n, k_max], last_token [n], cu_rows [n+1]")
+    if row_req.numel() != cap or row_pos.numel() != cap or packed_tokens.numel() != cap:
+        raise ValueError("row maps need n*(k_max+1) entries")
+
+
+def sv_budget_select_pack(conf, draft_len, cost, t_base, n_bonus, last_token, draft_tokens, kept,
+                          budget, cu_rows, row_req, row_pos, packed_tokens, survival=None,
+                          dev_error=None, stream=None, ws=None):
+    """sv_budget_select then sv_pack_varlen, one launch fewer (same tensors as the two)."""
+    for name, t, nd in (("conf", conf, 2), ("draft_len", draft_len, 1), ("cost", cost, 1),
+                        ("kept", kept, 1), ("budget", budget, 1)):
+        _dev(t, torch.float32 if name in ("conf", "cost") else torch.int32, name, nd)
+    _dev(survival, torch.float32, "survival", 2)
+    _dev(dev_error, torch.int32, "dev_error", 1)
+    _dev(ws, torch.uint8, "ws", 1)
+    n, k_max = conf.shape
+    if draft_len.numel() != n or kept.numel() != n or budget.numel() < 1:
+        raise ValueError("draft_len, kept must have n entries and budget one")
+    _pack_outputs(n, k_max, last_token, draft_tokens, cu_rows, row_req, row_pos, packed_tokens)
+    _check(_lib.sv_budget_select_pack(_ptr(conf), _ptr(draft_len), n, k_max, _ptr(cost),
+                                      cost.numel(), int(t_base), int(n_bonus), _ptr(last_token),
+                                      _ptr(draft_tokens), _ptr(kept), _ptr(budget),
+                                      _ptr(survival), _ptr(cu_rows), _ptr(row_req), _ptr(row_pos),
+                                      _ptr(packed_tokens), _ptr(dev_error), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(stream)),
+           "sv_budget_select_pack")
+
+
+def sv_budget_allocate_pack(conf, draft_len, budget_in, last_token, draft_tokens, kept, cu_rows,
+                            row_req, row_pos, packed_tokens, budget_used=None, survival=None,
+                            dev_error=None, stream=None, ws=None):
+    """sv_budget_allocate then sv_pack_varlen, one launch fewer."""
+    _dev(conf, torch.float32, "conf", 2)
+    for name, t in (("draft_len", draft_len), ("budget_in", budget_in), ("kept", kept),
+                    ("budget_used", budget_used), ("dev_error", dev_error)):
+        _dev(t, torch.int32, name, 1)
+    _dev(survival, torch.float32, "survival", 2)
+    _dev(ws, torch.uint8, "ws", 1)
+    n, k_max = conf.shape
+    if draft_len.numel() != n or kept.numel() != n or budget_in.numel() < 1:
+        raise ValueError("draft_len, kept must have n entries and budget_in one")
+    _pack_outputs(n, k_max, last_token, draft_tokens, cu_rows, row_req, row_pos, packed_tokens)
+    _check(_lib.sv_budget_allocate_pack(_ptr(conf), _ptr(draft_len), n, k_max, _ptr(budget_in),
+                                        _ptr(last_token), _ptr(draft_tokens), _ptr(kept),
+                                        _ptr(budget_used), _ptr(survival), _ptr(cu_rows),
+                                        _ptr(row_req), _ptr(row_pos), _ptr(packed_tokens),
+                                        _ptr(dev_error), _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream(stream)),
+           "sv_budget_allocate_pack")
 
 
 def sv_uniform_k_select(conf, draft_len, cost, t_base, n_bonus, kept, k_out, scores=None,

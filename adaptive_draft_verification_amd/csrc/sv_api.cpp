@@ -83,7 +83,48 @@ sv_status sv_budget_select(const float* conf, const int32_t* draft_len, int32_t 
     const size_t need = sv::budget_workspace_bytes(n_req, k_max);
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return SV_ERR_WORKSPACE;
     return launched(sv::launch_budget(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept,
-                                      budget, survival, dev_error, ws, as_stream(stream)));
+                                      budget, survival, dev_error, ws, nullptr,
+                                      as_stream(stream)));
+}
+
+// The outputs of sv_pack_varlen for the fused calls (sizes: the budget's).
+static sv_status check_pack_outputs(int32_t n_req, int32_t k_max, const int32_t* last_token,
+                                    const int32_t* draft_tokens, const int32_t* cu_rows,
+                                    const int32_t* row_req, const int32_t* row_pos,
+                                    const int32_t* packed_tokens) {
+    if (cu_rows == nullptr) return SV_ERR_NULL;
+    if (n_req > 0 && (last_token == nullptr || row_req == nullptr || row_pos == nullptr ||
+                      packed_tokens == nullptr))
+        return SV_ERR_NULL;
+    if (n_req > 0 && k_max > 0 && draft_tokens == nullptr) return SV_ERR_NULL;
+    return SV_OK;
+}
+
+sv_status sv_budget_select_pack(const float* conf, const int32_t* draft_len, int32_t n_req,
+                                int32_t k_max, const float* cost, int32_t cost_len,
+                                int32_t t_base, int32_t n_bonus, const int32_t* last_token,
+                                const int32_t* draft_tokens, int32_t* kept, int32_t* budget,
+                                float* survival, int32_t* cu_rows, int32_t* row_req,
+                                int32_t* row_pos, int32_t* packed_tokens, int32_t* dev_error,
+                                void* ws, size_t ws_bytes, void* stream) {
+    if (n_req < 0 || k_max < 0) return SV_ERR_SHAPE;
+    const sv_status ps = check_pack_outputs(n_req, k_max, last_token, draft_tokens, cu_rows,
+                                            row_req, row_pos, packed_tokens);
+    if (ps != SV_OK) return ps;
+    if (cost == nullptr || budget == nullptr) return SV_ERR_NULL;
+    if (n_req > 0 && (draft_len == nullptr || kept == nullptr)) return SV_ERR_NULL;
+    if (n_req > 0 && k_max > 0 && conf == nullptr) return SV_ERR_NULL;
+    if (n_req > SV_MAX_BUDGET_SLOTS || k_max > SV_MAX_DRAFT ||
+        (int64_t)n_req * k_max > SV_MAX_BUDGET_SLOTS)
+        return SV_ERR_SHAPE;
+    if (t_base < 0 || n_bonus < 0) return SV_ERR_VALUE;
+    if ((int64_t)cost_len < (int64_t)t_base + (int64_t)n_req * k_max + 1) return SV_ERR_SHAPE;
+    const size_t need = sv::budget_workspace_bytes(n_req, k_max);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return SV_ERR_WORKSPACE;
+    const sv::PackTargets pack{last_token, draft_tokens, cu_rows, row_req, row_pos, packed_tokens};
+    return launched(sv::launch_budget(conf, draft_len, n_req, k_max, cost, t_base, n_bonus, kept,
+                                      budget, survival, dev_error, ws, &pack,
+                                      as_stream(stream)));
 }
 
 sv_status sv_budget_allocate(const float* conf, const int32_t* draft_len, int32_t n_req,
@@ -100,7 +141,32 @@ sv_status sv_budget_allocate(const float* conf, const int32_t* draft_len, int32_
     const size_t need = sv::budget_workspace_bytes(n_req, k_max);
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return SV_ERR_WORKSPACE;
     return launched(sv::launch_allocate(conf, draft_len, n_req, k_max, budget_in, kept,
-                                        budget_used, survival, dev_error, ws,
+                                        budget_used, survival, dev_error, ws, nullptr,
+                                        as_stream(stream)));
+}
+
+sv_status sv_budget_allocate_pack(const float* conf, const int32_t* draft_len, int32_t n_req,
+                                  int32_t k_max, const int32_t* budget_in,
+                                  const int32_t* last_token, const int32_t* draft_tokens,
+                                  int32_t* kept, int32_t* budget_used, float* survival,
+                                  int32_t* cu_rows, int32_t* row_req, int32_t* row_pos,
+                                  int32_t* packed_tokens, int32_t* dev_error, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    if (n_req < 0 || k_max < 0) return SV_ERR_SHAPE;
+    const sv_status ps = check_pack_outputs(n_req, k_max, last_token, draft_tokens, cu_rows,
+                                            row_req, row_pos, packed_tokens);
+    if (ps != SV_OK) return ps;
+    if (budget_in == nullptr) return SV_ERR_NULL;
+    if (n_req > 0 && (draft_len == nullptr || kept == nullptr)) return SV_ERR_NULL;
+    if (n_req > 0 && k_max > 0 && conf == nullptr) return SV_ERR_NULL;
+    if (n_req > SV_MAX_BUDGET_SLOTS || k_max > SV_MAX_DRAFT ||
+        (int64_t)n_req * k_max > SV_MAX_BUDGET_SLOTS)
+        return SV_ERR_SHAPE;
+    const size_t need = sv::budget_workspace_bytes(n_req, k_max);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return SV_ERR_WORKSPACE;
+    const sv::PackTargets pack{last_token, draft_tokens, cu_rows, row_req, row_pos, packed_tokens};
+    return launched(sv::launch_allocate(conf, draft_len, n_req, k_max, budget_in, kept,
+                                        budget_used, survival, dev_error, ws, &pack,
                                         as_stream(stream)));
 }
 

@@ -203,10 +203,11 @@ struct BetterOp {
 
 // kept[r] = #{j : rank(r, j) < B}.  rk[q] holds the rank of slot
 // tid + 1024 q (slots past draft_len rank at `total` or later, never before
-// B <= total).  Every thread of the workgroup calls this (one barrier).
+// B <= total).  kept_s (LDS, or null) gets a copy.  Every thread of the
+// workgroup calls this (one barrier).
 __device__ __forceinline__ void write_kept(const int32_t* rk, int per, int B, int n_req,
                                            int k_max, uint8_t* in_budget,
-                                           int32_t* __restrict__ kept) {
+                                           int32_t* __restrict__ kept, uint8_t* kept_s) {
     const int tid = threadIdx.x;
     const int n_slots = n_req * k_max;
 #pragma unroll
@@ -220,13 +221,110 @@ __device__ __forceinline__ void write_kept(const int32_t* rk, int per, int B, in
         int k_in = 0;
         for (int j = 0; j < k_max; ++j) k_in += in_budget[r * k_max + j];
         kept[r] = k_in;
+        if (kept_s != nullptr) kept_s[r] = (uint8_t)k_in;
     }
 }
 
+// ------------------------------------------------- packing in the same launch
+// The varlen layout of sv_pack_varlen (agentlens page, section "기술적 구현
+// 및 CUDA Graphs", item Graph Capture; section "설정 및 재현": capacity
+// (k + 1) * n), written by the workgroup that has just counted the kept
+// slots, from its LDS copy of them: one launch fewer on the step's path.
+struct PackOut {
+    const int32_t* last_token;    // [n]
+    const int32_t* draft_tokens;  // [n, k_max]
+    int32_t* cu_rows;             // [n + 1]
+    int32_t* row_req;             // [n (k_max + 1)]
+    int32_t* row_pos;
+    int32_t* packed_tokens;
+};
+
+// Ids the packing will copy, loaded at the start of the kernel so that their
+// latency hides under the budget's own work: the draft id of slot
+// tid + 1024 q and the last token of request tid + 1024 q.
+struct PackIds {
+    int32_t dtok[kPerThread];
+    int32_t ltok[kPerThread];
+};
+
+__device__ __forceinline__ void pack_prefetch(const PackOut& po, int n_req, int k_max,
+                                              PackIds& ids) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int x = tid + q * kThreads;
+        ids.dtok[q] = x < n_req * k_max ? po.draft_tokens[x] : -1;
+        ids.ltok[q] = x < n_req ? po.last_token[x] : -1;
+    }
+}
+
+// Called by every thread after write_kept (kept_s complete in LDS).  cu_s:
+// LDS, n_req + 1 entries; wave_tot: LDS, kWaves entries.
+__device__ void pack_from_lds(const uint8_t* kept_s, int n_req, int k_max, const PackOut& po,
+                              const PackIds& ids, int32_t* cu_s, int32_t* wave_tot) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    // rows per request (kept + 1): thread t sums requests [t per, t per + per)
+    const int per = (n_req + kThreads - 1) / kThreads;
+    const int first = tid * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+        if (first + i < n_req) local += (int)kept_s[first + i] + 1;
+    const int incl = wave_incl_sum_dpp(local, lane);
+    if (lane == kWave - 1) wave_tot[wave] = incl;
+    __syncthreads();
+    int start = incl - local;
+    for (int v = 0; v < wave; ++v) start += wave_tot[v];
+    for (int i = 0; i < per; ++i) {
+        const int r = first + i;
+        if (r < n_req) {
+            cu_s[r] = start;
+            po.cu_rows[r] = start;
+            start += (int)kept_s[r] + 1;
+        }
+    }
+    int total = 0;
+    for (int v = 0; v < kWaves; ++v) total += wave_tot[v];
+    if (tid == 0) po.cu_rows[n_req] = total;
+    __syncthreads();
+    // row 0 of each request: its last token; row 1 + j: draft j, if kept
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int r = tid + q * kThreads;
+        if (r < n_req) {
+            const int row = cu_s[r];
+            po.row_req[row] = r;
+            po.row_pos[row] = 0;
+            po.packed_tokens[row] = ids.ltok[q];
+        }
+        const int x = tid + q * kThreads;
+        if (x < n_req * k_max) {
+            const int rr = x / k_max, j = x - rr * k_max;
+            if (j < (int)kept_s[rr]) {
+                const int row = cu_s[rr] + 1 + j;
+                po.row_req[row] = rr;
+                po.row_pos[row] = j + 1;
+                po.packed_tokens[row] = ids.dtok[q];
+            }
+        }
+    }
+    const int cap = n_req * (k_max + 1);
+    for (int row = total + tid; row < cap; row += kThreads) {
+        po.row_req[row] = -1;
+        po.row_pos[row] = -1;
+        po.packed_tokens[row] = -1;
+    }
+}
+
+template <bool PACK>
 __global__ __launch_bounds__(kThreads) void finish_kernel(
     int n_req, int k_max, const float* __restrict__ cost, int t_base, int n_bonus,
-    int32_t* __restrict__ kept, int32_t* __restrict__ budget, int32_t* dev_error, void* ws) {
+    int32_t* __restrict__ kept, int32_t* __restrict__ budget, int32_t* dev_error, void* ws,
+    PackOut po) {
     __shared__ uint8_t in_budget[SV_MAX_BUDGET_SLOTS];
+    __shared__ uint8_t kept_s[PACK ? SV_MAX_BUDGET_SLOTS : 1];
+    __shared__ int32_t cu_s[PACK ? SV_MAX_BUDGET_SLOTS : 1];
+    __shared__ int32_t pack_tot[kWaves];
     __shared__ uint64_t wave_tot[kWaves];
     __shared__ Cand wave_best[kWaves];
     __shared__ int32_t best_b_s;
@@ -262,6 +360,8 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     const float cost0 = cost[t_base];
     const int total = n_slots > 0 ? w.total[0] : 0;
     if (tid == 0) err_s = 0;
+    PackIds ids;
+    if (PACK) pack_prefetch(po, n_req, k_max, ids);
 
     uint64_t fx[kPerThread];
     uint64_t local = 0;
@@ -313,10 +413,14 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     }
     __syncthreads();
     const int B = best_b_s;
-    write_kept(rk, per, B, n_req, k_max, in_budget, kept);
+    write_kept(rk, per, B, n_req, k_max, in_budget, kept, PACK ? kept_s : nullptr);
     if (tid == 0) {
         budget[0] = B;
         raise_error(dev_error, err_s);
+    }
+    if (PACK) {
+        __syncthreads();
+        pack_from_lds(kept_s, n_req, k_max, po, ids, cu_s, pack_tot);
     }
 }
 
@@ -324,12 +428,19 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
 // 신뢰도 스케줄링 메커니즘", item Execution Pipeline: B comes from the
 // previous step's confidences, the slots from the current ones): the first
 // min(max(B, 0), total) slots of the rank kernel's order.  One workgroup.
+template <bool PACK>
 __global__ __launch_bounds__(kThreads) void allocate_kernel(int n_req, int k_max,
                                                             const int32_t* __restrict__ budget_in,
                                                             int32_t* __restrict__ kept,
-                                                            int32_t* budget_used, void* ws) {
+                                                            int32_t* budget_used, void* ws,
+                                                            PackOut po) {
     __shared__ uint8_t in_budget[SV_MAX_BUDGET_SLOTS];
+    __shared__ uint8_t kept_s[PACK ? SV_MAX_BUDGET_SLOTS : 1];
+    __shared__ int32_t cu_s[PACK ? SV_MAX_BUDGET_SLOTS : 1];
+    __shared__ int32_t pack_tot[kWaves];
     const int tid = threadIdx.x;
+    PackIds ids;
+    if (PACK) pack_prefetch(po, n_req, k_max, ids);
     const int n_slots = n_req * k_max;
     const BudgetWs w = budget_ws(ws, n_slots);
     const int per = (n_slots + kThreads - 1) / kThreads;
@@ -344,8 +455,12 @@ __global__ __launch_bounds__(kThreads) void allocate_kernel(int n_req, int k_max
     const int total = n_slots > 0 ? w.total[0] : 0;
     const int b_in = budget_in[0];
     const int B = b_in < 0 ? 0 : (b_in > total ? total : b_in);
-    write_kept(rk, per, B, n_req, k_max, in_budget, kept);
+    write_kept(rk, per, B, n_req, k_max, in_budget, kept, PACK ? kept_s : nullptr);
     if (tid == 0 && budget_used != nullptr) budget_used[0] = B;
+    if (PACK) {
+        __syncthreads();
+        pack_from_lds(kept_s, n_req, k_max, po, ids, cu_s, pack_tot);
+    }
 }
 
 // One draft length for the whole batch ("Hardware-Aware Dynamic Speculative
@@ -472,23 +587,38 @@ hipError_t launch_rank(const float* conf, const int32_t* draft_len, int n_req, i
 hipError_t launch_budget(const float* conf, const int32_t* draft_len, int n_req, int k_max,
                          const float* cost, int t_base, int n_bonus, int32_t* kept,
                          int32_t* budget, float* survival, int32_t* dev_error, void* ws,
-                         hipStream_t stream) {
+                         const PackTargets* pack, hipStream_t stream) {
     const hipError_t e = launch_rank(conf, draft_len, n_req, k_max, survival, dev_error, ws,
                                      stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kThreads), 0, stream, n_req, k_max, cost,
-                       t_base, n_bonus, kept, budget, dev_error, ws);
+    if (pack != nullptr) {
+        const PackOut po{pack->last_token, pack->draft_tokens, pack->cu_rows,
+                         pack->row_req,    pack->row_pos,      pack->packed_tokens};
+        hipLaunchKernelGGL(finish_kernel<true>, dim3(1), dim3(kThreads), 0, stream, n_req, k_max,
+                           cost, t_base, n_bonus, kept, budget, dev_error, ws, po);
+    } else {
+        hipLaunchKernelGGL(finish_kernel<false>, dim3(1), dim3(kThreads), 0, stream, n_req,
+                           k_max, cost, t_base, n_bonus, kept, budget, dev_error, ws, PackOut{});
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_allocate(const float* conf, const int32_t* draft_len, int n_req, int k_max,
                            const int32_t* budget_in, int32_t* kept, int32_t* budget_used,
-                           float* survival, int32_t* dev_error, void* ws, hipStream_t stream) {
+                           float* survival, int32_t* dev_error, void* ws,
+                           const PackTargets* pack, hipStream_t stream) {
     const hipError_t e = launch_rank(conf, draft_len, n_req, k_max, survival, dev_error, ws,
                                      stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(allocate_kernel, dim3(1), dim3(kThreads), 0, stream, n_req, k_max,
-                       budget_in, kept, budget_used, ws);
+    if (pack != nullptr) {
+        const PackOut po{pack->last_token, pack->draft_tokens, pack->cu_rows,
+                         pack->row_req,    pack->row_pos,      pack->packed_tokens};
+        hipLaunchKernelGGL(allocate_kernel<true>, dim3(1), dim3(kThreads), 0, stream, n_req,
+                           k_max, budget_in, kept, budget_used, ws, po);
+    } else {
+        hipLaunchKernelGGL(allocate_kernel<false>, dim3(1), dim3(kThreads), 0, stream, n_req,
+                           k_max, budget_in, kept, budget_used, ws, PackOut{});
+    }
     return hipGetLastError();
 }
 

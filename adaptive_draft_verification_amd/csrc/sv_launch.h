@@ -10,13 +10,24 @@
 
 namespace sv {
 
+// Outputs of sv_pack_varlen, written by the budget's last kernel when given.
+struct PackTargets {
+    const int32_t* last_token;
+    const int32_t* draft_tokens;
+    int32_t* cu_rows;
+    int32_t* row_req;
+    int32_t* row_pos;
+    int32_t* packed_tokens;
+};
+
 hipError_t launch_budget(const float* conf, const int32_t* draft_len, int n_req, int k_max,
                          const float* cost, int t_base, int n_bonus, int32_t* kept,
                          int32_t* budget, float* survival, int32_t* dev_error, void* ws,
-                         hipStream_t stream);
+                         const PackTargets* pack, hipStream_t stream);
 hipError_t launch_allocate(const float* conf, const int32_t* draft_len, int n_req, int k_max,
                            const int32_t* budget_in, int32_t* kept, int32_t* budget_used,
-                           float* survival, int32_t* dev_error, void* ws, hipStream_t stream);
+                           float* survival, int32_t* dev_error, void* ws,
+                           const PackTargets* pack, hipStream_t stream);
 size_t budget_workspace_bytes(int n_req, int k_max);
 
 hipError_t launch_uniform_k(const float* conf, const int32_t* draft_len, int n_req, int k_max,

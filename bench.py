@@ -1,7 +1,8 @@
 """Benchmark of the verify step on one MI355X.
 
 A step is one pass of the whole path on one batch: adaptive budget selection
-(sv_budget_select), varlen packing (sv_pack_varlen) and full-vocabulary
+and varlen packing (sv_budget_select_pack: the two in one launch fewer;
+--separate-pack calls sv_budget_select and sv_pack_varlen) and full-vocabulary
 verification (sv_verify: row statistics, then one workgroup per request that
 decides and draws), each stage reading the previous stage's device output.
 The default workload is 256 requests with 7 drafts each over a 129280-token
@@ -66,6 +67,9 @@ def parse():
                     help="time eagerly launched steps (default)")
     ap.add_argument("--graphs", type=int, default=4,
                     help="graphs captured (one per replica and Philox step), replayed in turn")
+    ap.add_argument("--separate-pack", action="store_true",
+                    help="budget and pack as two calls (sv_budget_select, sv_pack_varlen) "
+                         "instead of sv_budget_select_pack")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only copy a device buffer of this many MiB three times and exit: "
                          "a plain copy of known size, to scale HBM byte counters by")
@@ -214,12 +218,18 @@ def main():
                 events[k].record(stream)
 
         mark(0)
-        if kept_in is None:
+        if kept_in is None and args.separate_pack:
             sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, kept, budget,
                                 survival, err, ws=bws)
-        mark(1)
-        if kept_in is None:
+            mark(1)
             sv.sv_pack_varlen(kept, last_d, toks_d, cu, row_req, row_pos, packed, err)
+        elif kept_in is None:  # budget and pack in one launch fewer
+            sv.sv_budget_select_pack(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, last_d, toks_d,
+                                     kept, budget, cu, row_req, row_pos, packed, survival, err,
+                                     ws=bws)
+            mark(1)
+        else:
+            mark(1)
         mark(2)
         for stage in (1, 2):
             sv.sv_verify_stages(tp, dr, toks_d, cu_i, mode, w.tau, w.seed, i, tok_out, acc_out,
@@ -448,6 +458,7 @@ def main():
                      "traffic": traffic, "kernel": "rowstats_kernel (verify pass 1)",
                      "bytes_per_launch": int(pass1_bytes),
                      "launch_us": round(roof_ms * 1e3, 2)},
+        "budget_pack": "separate" if args.separate_pack else "fused",
         "budget_select_us": round(float(np.mean(stage_ms[:, 0])) * 1e3, 2),
         "budget_allocate_us": budget_allocate_us,
         "pack_us": round(float(np.mean(stage_ms[:, 1])) * 1e3, 2),

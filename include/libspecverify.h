@@ -174,6 +174,30 @@ sv_status sv_budget_allocate(const float* conf, const int32_t* draft_len, int32_
                              size_t ws_bytes, void* stream);
 
 /*
+ * sv_budget_select_pack, sv_budget_allocate_pack — sv_budget_select (or
+ * sv_budget_allocate) followed by sv_pack_varlen in one launch fewer: the
+ * workgroup that counts the kept slots also writes the packed layout
+ * (cu_rows, row_req, row_pos, packed_tokens exactly as sv_pack_varlen
+ * documents them, from the kept counts it has just computed, which are
+ * always inside [0, k_max]).  Arguments, sizes, workspace and errors: the
+ * union of the two calls' (the budget's limits apply).
+ */
+sv_status sv_budget_select_pack(const float* conf, const int32_t* draft_len, int32_t n_req,
+                                int32_t k_max, const float* cost, int32_t cost_len,
+                                int32_t t_base, int32_t n_bonus, const int32_t* last_token,
+                                const int32_t* draft_tokens, int32_t* kept, int32_t* budget,
+                                float* survival, int32_t* cu_rows, int32_t* row_req,
+                                int32_t* row_pos, int32_t* packed_tokens, int32_t* dev_error,
+                                void* ws, size_t ws_bytes, void* stream);
+sv_status sv_budget_allocate_pack(const float* conf, const int32_t* draft_len, int32_t n_req,
+                                  int32_t k_max, const int32_t* budget_in,
+                                  const int32_t* last_token, const int32_t* draft_tokens,
+                                  int32_t* kept, int32_t* budget_used, float* survival,
+                                  int32_t* cu_rows, int32_t* row_req, int32_t* row_pos,
+                                  int32_t* packed_tokens, int32_t* dev_error, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
  * sv_uniform_k_select — one draft length K for the whole batch, by goodput.
  *
  * "Hardware-Aware Dynamic Speculative Decoding (DSD), feat. Cohere", section

@@ -112,6 +112,37 @@ def test_budget_allocate_host_validation():
     assert allocate(ws_bytes=sv.sv_budget_workspace_bytes(4, 3) - 1) == sv.SV_ERR_WORKSPACE
 
 
+def select_pack(**kw):
+    args = dict(conf=FAKE, draft_len=FAKE, n_req=4, k_max=3, cost=FAKE, cost_len=17, t_base=4,
+                n_bonus=4, last_token=FAKE, draft_tokens=FAKE, kept=FAKE, budget=FAKE,
+                survival=None, cu_rows=FAKE, row_req=FAKE, row_pos=FAKE, packed=FAKE,
+                dev_error=None, ws=FAKE, ws_bytes=sv.sv_budget_workspace_bytes(4, 3), stream=None)
+    args.update(kw)
+    return sv._lib.sv_budget_select_pack(*args.values())
+
+
+def allocate_pack(**kw):
+    args = dict(conf=FAKE, draft_len=FAKE, n_req=4, k_max=3, budget_in=FAKE, last_token=FAKE,
+                draft_tokens=FAKE, kept=FAKE, budget_used=None, survival=None, cu_rows=FAKE,
+                row_req=FAKE, row_pos=FAKE, packed=FAKE, dev_error=None, ws=FAKE,
+                ws_bytes=sv.sv_budget_workspace_bytes(4, 3), stream=None)
+    args.update(kw)
+    return sv._lib.sv_budget_allocate_pack(*args.values())
+
+
+def test_fused_budget_pack_host_validation():
+    for call, own in ((select_pack, ("cost", "budget")), (allocate_pack, ("budget_in",))):
+        for key in own + ("conf", "draft_len", "kept", "last_token", "draft_tokens", "cu_rows",
+                          "row_req", "row_pos", "packed"):
+            assert call(**{key: None}) == sv.SV_ERR_NULL, (call.__name__, key)
+        assert call(n_req=-1) == sv.SV_ERR_SHAPE
+        assert call(n_req=2048, k_max=5) == sv.SV_ERR_SHAPE
+        assert call(n_req=1, k_max=65) == sv.SV_ERR_SHAPE
+        assert call(ws=None) == sv.SV_ERR_WORKSPACE
+    assert select_pack(cost_len=16) == sv.SV_ERR_SHAPE
+    assert select_pack(t_base=-1) == sv.SV_ERR_VALUE
+
+
 def test_budget_select_host_validation():
     assert budget(cost_len=16) == sv.SV_ERR_SHAPE          # needs t_base + n*k + 1
     assert budget(n_req=-1) == sv.SV_ERR_SHAPE

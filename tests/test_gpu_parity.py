@@ -228,6 +228,81 @@ def test_allocate_graph_replay_follows_the_budget_in_memory():
         np.testing.assert_array_equal(kept.cpu().numpy(), o["kept"])
 
 
+# ------------------------------------------ budget and pack in one launch fewer
+
+def check_fused_pack(conf, dl, k, cost=None, t_base=0, n_bonus=0, budget=None, seed=0):
+    """sv_budget_select_pack (cost given) or sv_budget_allocate_pack (budget
+    given) against the oracle's budget and pack, every output bit for bit."""
+    import adaptive_draft_verification_amd as sv
+    rng = np.random.default_rng(seed)
+    n = len(dl)
+    last = rng.integers(0, 50000, n).astype(np.int32)
+    toks = rng.integers(0, 50000, (n, k)).astype(np.int32)
+    cap = n * (k + 1)
+    kept = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    b = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    surv = torch.empty(n, k, dtype=torch.float32, device="cuda")
+    cu = torch.full((n + 1,), -7, dtype=torch.int32, device="cuda")
+    rr, rp, pt = (torch.full((cap,), -7, dtype=torch.int32, device="cuda") for _ in range(3))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, sv.sv_budget_workspace_bytes(n, k)), dtype=torch.uint8,
+                     device="cuda")
+    args = (to_dev(last), to_dev(toks))
+    if budget is None:
+        sv.sv_budget_select_pack(to_dev(conf), to_dev(dl), to_dev(cost), t_base, n_bonus, *args,
+                                 kept, b, cu, rr, rp, pt, surv, err, ws=ws)
+        o = oracle.budget_select(conf, dl, k, cost, t_base, n_bonus)
+        want_b = o["budget"]
+    else:
+        sv.sv_budget_allocate_pack(to_dev(conf), to_dev(dl), to_dev(np.array([budget], np.int32)),
+                                   *args, kept, cu, rr, rp, pt, b, surv, err, ws=ws)
+        o = oracle.budget_allocate(conf, dl, k, budget)
+        want_b = o["budget_used"]
+    torch.cuda.synchronize()
+    op = oracle.pack_varlen(o["kept"], last, toks, k)
+    np.testing.assert_array_equal(kept.cpu().numpy(), o["kept"])
+    assert int(b.cpu()[0]) == want_b
+    np.testing.assert_array_equal(surv.cpu().numpy().view(np.uint32), o["survival"].view(np.uint32))
+    for key, t in (("cu_rows", cu), ("row_req", rr), ("row_pos", rp), ("packed_tokens", pt)):
+        np.testing.assert_array_equal(t.cpu().numpy(), op[key], err_msg=key)
+    assert int(err.cpu()[0]) == o["dev_error"] | op["dev_error"]
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_budget_select_pack_random(seed):
+    rng = np.random.default_rng(900 + seed)
+    n = int(rng.integers(1, 300))
+    k = int(rng.integers(1, min(16, 8192 // n) + 1))
+    conf, dl, cost, t_base, n_bonus = workloads.random_budget_case(
+        rng, n, k, ties=seed % 2 == 0, zeros=seed % 3 == 0, flat_cost=seed % 5 == 0)
+    if seed % 7 == 0:
+        dl[0] = k + 3
+        dl[-1] = -1
+    check_fused_pack(conf, dl, k, cost, t_base, n_bonus, seed=seed)
+    total = int(np.clip(dl, 0, k).sum())
+    for B in (-2, 0, total // 3, total + 4):
+        check_fused_pack(conf, dl, k, budget=B, seed=seed)
+
+
+@pytest.mark.parametrize("n,k", [(8192, 1), (1024, 8), (128, 64), (4096, 2), (1, 1), (3, 0),
+                                 (0, 4)])
+def test_budget_pack_fused_edges(n, k):
+    rng = np.random.default_rng(n + 7 * k)
+    conf = rng.uniform(0.3, 1.0, (n, k)).astype(np.float32)
+    dl = rng.integers(0, k + 1, n).astype(np.int32)
+    t = np.arange(n + n * k + 1, dtype=np.float32)
+    cost = np.maximum(1.0, t / max(1, n)).astype(np.float32)
+    check_fused_pack(conf, dl, k, cost, n, n)
+    check_fused_pack(conf, dl, k, budget=n * k // 2)
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
+def test_budget_select_pack_workloads(name):
+    w = workloads.make(name)
+    cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+    check_fused_pack(w.conf, w.draft_len, w.k_max, cost, w.t_base, w.n_bonus)
+
+
 # ------------------------------------------------------- uniform draft length
 
 @pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
