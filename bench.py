@@ -10,9 +10,11 @@ vocabulary, bf16 logits, confidences X^j with X ~ Beta(8, 2), and a cost
 table padded to multiples of 16 tokens (workloads.make("b256_v129280")); the
 budget decides how many rows each request verifies.
 
-Inputs are generated once on the host and copied to HBM before timing; two
-replicas of the logit buffers alternate between steps so that reads come from
-HBM rather than the 256 MB Infinity Cache.  The headline times K steps
+Inputs are generated once on the host and copied to HBM before timing; four
+replicas of the logit buffers (about 1 GB each) rotate between steps so that
+reads come from HBM rather than the 256 MB Infinity Cache: with two, the rows
+a draw re-read two steps earlier could still be cached when pass 1 streams
+that replica again.  The headline times K steps
 launched back to back (--graph replays them from HIP graphs instead, one per
 replica and Philox step, in turn); `value` is target rows verified per second
 of that wall time.  A separate loop with HIP events on the launch stream times
@@ -55,7 +57,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="b256_v129280")
     ap.add_argument("--mode", choices=["stochastic", "greedy"], default="stochastic")
-    ap.add_argument("--replicas", type=int, default=2)
+    ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--full-k-iters", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -347,9 +349,8 @@ def main():
         full_idx = np.concatenate([r * (K + 1) + np.arange(int(w.draft_len[r]) + 1)
                                    for r in range(n)])
         tgt_packed = tgt_full_d.index_select(0, d(full_idx.astype(np.int64)))
-        full_reps = [(tgt_packed, drf_full_d)]
-        if args.replicas > 1:
-            full_reps.append((tgt_packed.clone(), replicas[1][1]))
+        full_reps = [(tgt_packed if i == 0 else tgt_packed.clone(), replicas[i][1])
+                     for i in range(args.replicas)]
         rows_tf = int(cu_full[-1].item())
         rows_df = int(w.draft_len.sum())
         kw = dict(reps=full_reps, cu_rows=cu_full, kept_in=True)
