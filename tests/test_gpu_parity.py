@@ -467,6 +467,38 @@ def test_verify_ragged_vocab_and_strides(dtype, V, ld_pad, mode):
                    3, 11)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("mode", ["stochastic", "greedy"])
+@pytest.mark.parametrize("which", ["vocab", "drafts"])
+def test_verify_maximum_sizes(which, dtype, mode):
+    """The largest vocabulary (SV_MAX_VOCAB: 8 row parts, the most super-
+    groups per draw) and the largest draft count (SV_MAX_DRAFT: one wave64
+    ballot per request), with a request that keeps every draft, one that keeps
+    some and one that keeps none."""
+    import adaptive_draft_verification_amd as sv
+    rng = np.random.default_rng(2024)
+    if which == "vocab":
+        n, k, V, kept = 3, 3, sv.SV_MAX_VOCAB, [3, 1, 0]
+    else:
+        n, k, V, kept = 3, sv.SV_MAX_DRAFT, 20001, [sv.SV_MAX_DRAFT, 17, 0]
+    target, draft, toks, cu = synthetic(rng, n, k, V, kept)
+    if dtype == torch.bfloat16:
+        target, draft = bf16_round(target), bf16_round(draft)
+    log(f"maximum {which}: V={V} k={k} {dtype} {mode}: rows={int(cu[-1])}")
+    dmode = draft if mode == "stochastic" else None
+    g = gpu_verify(target, dmode, toks, cu, k, mode, 1.0, dtype, seed=13, step=5, features=True)
+    compare_verify(g, target, dmode, toks, cu, k, V, mode, 1.0, 13, 5)
+
+
+def test_verify_many_small_requests():
+    rng = np.random.default_rng(77)
+    n, k, V = 4096, 2, 1000
+    target, draft, toks, cu = synthetic(rng, n, k, V)
+    g = gpu_verify(target, draft, toks, cu, k, "stochastic", 0.9, torch.float32, seed=1, step=2,
+                   features=True)
+    compare_verify(g, target, draft, toks, cu, k, V, "stochastic", 0.9, 1, 2)
+
+
 @pytest.mark.parametrize("mode", ["stochastic", "greedy"])
 def test_verify_no_drafts(mode):
     rng = np.random.default_rng(5)
