@@ -1077,14 +1077,76 @@ __device__ __forceinline__ void pass1_slot(int g, int n_req, int k_max, bool gre
 #endif
 }
 
+// Dense pass-1 order: with well-formed row offsets (cu_rows[0] = 0, every
+// kept count in [0, k_max], the last offset within target_rows) workgroup u
+// takes the u-th existing row part — target rows in packed order, then draft
+// rows request by request — found by a binary search of the offsets staged in
+// LDS, so every workgroup past the kept rows sits at the end of the grid.
+// Other offsets (and batches above kDenseMaxReq requests) keep the
+// (position, request) order of pass1_slot, whose checks reject bad offsets
+// request by request.
+#ifndef SV_PASS1_DENSE
+#define SV_PASS1_DENSE 1
+#endif
+constexpr int kDenseMaxReq = 512;  // each workgroup stages n + 1 offsets
+
+// Largest i in [0, n] with key(i) <= x, key non-decreasing and key(0) <= x:
+// two wave-wide steps (each lane tests one candidate, a ballot counts).
+template <typename Key>
+__device__ __forceinline__ int last_at_most(int n, int x, Key key) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int step = (n + kWave) / kWave;  // 64 * step > n
+    int i1 = lane * step;
+    const uint64_t m1 = __ballot(i1 <= n && key(i1 <= n ? i1 : n) <= x);
+    const int base = (__popcll(m1) - 1) * step;  // key(base) <= x < key(base + step)
+    const int i2 = base + lane;
+    const uint64_t m2 = __ballot(lane < step && i2 <= n && key(i2 <= n ? i2 : n) <= x);
+    return base + __popcll(m2) - 1;
+}
+
 template <sv_dtype DT, bool GREEDY, bool FEAT>
 __global__ __launch_bounds__(kThreads) void rowstats_kernel(Args a, int n_req, int parts) {
     __shared__ float redf[4 * (kThreads / kWave)];
     __shared__ int redi[2 * (kThreads / kWave)];
+    __shared__ int32_t cu_s[SV_PASS1_DENSE ? kDenseMaxReq + 1 : 1];
     const int h = blockIdx.x % parts;
-    int r, slot;
-    pass1_slot(blockIdx.x / parts, n_req, a.k_max, GREEDY, &r, &slot);
-    const int lo = a.cu_rows[r], hi = a.cu_rows[r + 1];
+    int r, slot, lo, hi;
+    bool dense = false;
+    if (SV_PASS1_DENSE && n_req <= kDenseMaxReq) {
+        // one barrier: each thread checks the offsets it stages
+        int bad = 0;
+        for (int i = threadIdx.x; i <= n_req; i += kThreads) {
+            const int v = a.cu_rows[i];
+            cu_s[i] = v;
+            if (i == 0) bad |= v != 0;
+            if (i == n_req) bad |= (int64_t)v > a.target_rows;
+            if (i < n_req) {
+                const int b = a.cu_rows[i + 1] - v - 1;
+                bad |= b < 0 || b > a.k_max;
+            }
+        }
+        dense = !__syncthreads_or(bad);
+    }
+    if (dense) {
+        const int unit = blockIdx.x / parts;
+        const int rows_t = cu_s[n_req], rows_d = rows_t - n_req;
+        if (unit < rows_t) {  // target row `unit`
+            r = last_at_most(n_req, unit, [&](int i) { return cu_s[i]; });
+            slot = unit - cu_s[r];
+        } else if (!GREEDY && unit < rows_t + rows_d) {  // draft row `unit - rows_t`
+            const int d = unit - rows_t;
+            r = last_at_most(n_req, d, [&](int i) { return cu_s[i] - i; });
+            slot = a.k_max + 1 + (d - (cu_s[r] - r));
+        } else {
+            return;
+        }
+        lo = cu_s[r];
+        hi = cu_s[r + 1];
+    } else {
+        pass1_slot(blockIdx.x / parts, n_req, a.k_max, GREEDY, &r, &slot);
+        lo = a.cu_rows[r];
+        hi = a.cu_rows[r + 1];
+    }
     const int b = hi - lo - 1;
     if (lo < 0 || b < 0 || b > a.k_max || (int64_t)hi > a.target_rows) return;
     const bool is_draft = slot > a.k_max;
