@@ -43,8 +43,11 @@ namespace {
 
 // Launch shapes (overridable at build time for tuning sweeps).  Measured on
 // MI355X, 256 requests x 8 rows x 129280 bf16: non-temporal pass-1 loads move
-// the stream from ~5.8 to ~6.8 TB/s; 512-thread rows edge out 256 and 1024;
-// draw super-groups of 2 x 512 ids per wave beat 4 x 512 (35 vs 37 us).
+// the stream from ~5.8 to ~6.5 TB/s; 512-thread workgroups beat 256 and 1024;
+// with the dense order, parts of up to 131072 ids (one per row here) beat
+// 65536 (74.7 vs 76.8 us) and smaller parts lose more (3 parts 81, 4 parts
+// 88 us); an unroll of 8 loses to 4; draw super-groups of 2 x 512 ids per
+// wave beat 4 x 512 (35 vs 37 us).
 #ifndef SV_PASS1_THREADS
 #define SV_PASS1_THREADS 512
 #endif
@@ -464,7 +467,7 @@ struct alignas(8) FeatPart {
 };
 constexpr int kMaxParts = 8;
 #ifndef SV_PART_IDS
-#define SV_PART_IDS 65536
+#define SV_PART_IDS 131072
 #endif
 constexpr int kPartIds = SV_PART_IDS;  // parts of about this many ids
 

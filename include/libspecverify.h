@@ -311,7 +311,7 @@ sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
  *                first launch to the second).  Calls that overlap in time
  *                must not share a workspace.
  * Launch: two kernels.  Pass 1: one 512-thread workgroup per candidate row
- * part, rows cut into ceil(vocab / 65536) <= 8 parts (n_req * (2*k_max + 1)
+ * part, rows cut into ceil(vocab / 131072) <= 8 parts (n_req * (2*k_max + 1)
  * rows stochastic, n_req * (k_max + 1) greedy; rows beyond a request's kept
  * count do nothing).  Pass 2: one workgroup per request (1024 threads
  * stochastic, 64 greedy) merges the parts, decides and draws.

@@ -451,7 +451,7 @@ def bf16_round(a):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("V,ld_pad", [(1003, 0), (20001, 0), (32, 3), (8192 * 3 + 5, 1),
-                                      (1, 0), (7, 0)])
+                                      (1, 0), (7, 0), (131073, 1), (400003, 0)])
 @pytest.mark.parametrize("mode", ["stochastic", "greedy"])
 def test_verify_ragged_vocab_and_strides(dtype, V, ld_pad, mode):
     rng = np.random.default_rng(V + ld_pad)
@@ -488,6 +488,21 @@ def test_verify_maximum_sizes(which, dtype, mode):
     dmode = draft if mode == "stochastic" else None
     g = gpu_verify(target, dmode, toks, cu, k, mode, 1.0, dtype, seed=13, step=5, features=True)
     compare_verify(g, target, dmode, toks, cu, k, V, mode, 1.0, 13, 5)
+
+
+@pytest.mark.parametrize("n", [512, 513])
+def test_verify_dense_order_limit(n):
+    """512 requests take the dense pass-1 order, 513 the per-request one."""
+    rng = np.random.default_rng(n)
+    k, V = 3, 3001
+    target, draft, toks, cu = synthetic(rng, n, k, V)
+    for mode in ("stochastic", "greedy"):
+        dmode = draft if mode == "stochastic" else None
+        g = gpu_verify(target, dmode, toks, cu, k, mode, 1.1, torch.bfloat16 if n == 512 else
+                       torch.float32, seed=4, step=1, features=True)
+        t = bf16_round(target) if n == 512 else target
+        d = (bf16_round(draft) if n == 512 else draft) if dmode is not None else None
+        compare_verify(g, t, d, toks, cu, k, V, mode, 1.1, 4, 1)
 
 
 def test_verify_many_small_requests():
