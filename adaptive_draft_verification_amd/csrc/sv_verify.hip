@@ -601,12 +601,6 @@ struct GroupRaw {
     Raw8<DT> p[Geom<DT>::kU], q[Geom<DT>::kU];
 };
 
-// True if super-group g lies wholly inside the row and both rows are aligned.
-template <sv_dtype DT>
-__device__ __forceinline__ bool group_fast(const DrawRow& d, int g) {
-    return d.aligned && (g + 1) * Geom<DT>::kIds <= (d.vocab & ~7);
-}
-
 template <sv_dtype DT, bool RESID>
 __device__ __forceinline__ void group_fetch(const DrawRow& d, int g, int lane,
                                             GroupRaw<DT, RESID>& r) {
@@ -677,22 +671,35 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
     if (tid == 0) sm.next = kP2Waves;
     __syncthreads();
     {
-        int g = wave;  // the first claim of each wave is implicit
-        GroupRaw<DT, RESID> cur;
-        bool cur_fast = g < n_groups && group_fast<DT>(d, g);
-        if (cur_fast) group_fetch<DT, RESID>(d, g, lane, cur);
-        while (g < n_groups) {
+        // super-groups [0, n_fast) lie wholly inside an aligned row: a tight
+        // loop with two register buffers in turn; the rest (the row's last,
+        // partial super-group, or every one of an unaligned row) element-wise
+        const int n_fast = d.aligned ? (d.vocab & ~7) / kGroupIds : 0;
+        auto claim = [&]() {
             int g2 = 0;
             if (lane == 0) g2 = atomicAdd(&sm.next, 1);
-            g2 = __builtin_amdgcn_readfirstlane(g2);
-            GroupRaw<DT, RESID> nxt;
-            const bool nxt_fast = g2 < n_groups && group_fast<DT>(d, g2);
-            if (nxt_fast) group_fetch<DT, RESID>(d, g2, lane, nxt);
-            const float gs = wave_sum_dpp(group_lane_sum<DT, RESID>(d, g, lane, cur_fast, cur), lane);
+            return __builtin_amdgcn_readfirstlane(g2);
+        };
+        int g = wave;  // the first claim of each wave is implicit
+        GroupRaw<DT, RESID> ba, bb;
+        if (g < n_fast) group_fetch<DT, RESID>(d, g, lane, ba);
+        while (g < n_fast) {
+            int g2 = claim();
+            if (g2 < n_fast) group_fetch<DT, RESID>(d, g2, lane, bb);
+            float gs = wave_sum_dpp(group_lane_sum<DT, RESID>(d, g, lane, true, ba), lane);
             if (lane == 0) sm.gsum[g] = gs;
             g = g2;
-            cur = nxt;
-            cur_fast = nxt_fast;
+            if (g >= n_fast) break;
+            g2 = claim();
+            if (g2 < n_fast) group_fetch<DT, RESID>(d, g2, lane, ba);
+            gs = wave_sum_dpp(group_lane_sum<DT, RESID>(d, g, lane, true, bb), lane);
+            if (lane == 0) sm.gsum[g] = gs;
+            g = g2;
+        }
+        while (g < n_groups) {
+            const float gs = wave_sum_dpp(group_lane_sum<DT, RESID>(d, g, lane, false, ba), lane);
+            if (lane == 0) sm.gsum[g] = gs;
+            g = claim();
         }
     }
     __syncthreads();
