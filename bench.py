@@ -27,8 +27,11 @@ every draft (full K: 2048 target + 1792 draft rows) for the bandwidth figure
 at the largest size.  Two smaller legs time pass 1 with the draft-row
 features (entropy, largest probability) accumulated as well, and the one-K-
 per-batch selection (sv_uniform_k_select), and the allocation of a budget
-sized one step ahead (sv_budget_allocate).  The CPU oracle runs whole steps of
-the same workload on the host for the cpu_baseline figure.
+sized one step ahead (sv_budget_allocate).  Before the GPU is touched, the CPU
+oracle runs whole steps of the same workload on the host for the cpu_baseline
+figure: half the time on one thread, half with each step's requests spread
+over a pool of worker processes (the reported value; the one-thread rate is in
+its sample text).
 
 Prints one JSON line.
 """
@@ -60,7 +63,7 @@ def parse():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--full-k-iters", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="lower bound on the oracle's timed host work")
     ap.add_argument("--graph", dest="graph", action="store_true", default=False,
                     help="time steps replayed from HIP graphs (slower than eager launches "
@@ -119,6 +122,85 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
+# Inputs the forked oracle workers read (set before the pool forks; the
+# workers only read them, so the pages are shared, not copied).
+_CPU = {}
+
+
+def _oracle_requests(job):
+    """Oracle verify of requests [r0, r1) of one step (a pool worker's share)."""
+    import oracle
+    r0, r1, step = job
+    c = _CPU
+    K, V = c["K"], c["V"]
+    rows = 0
+    for r in range(r0, r1):
+        b = int(c["kept"][r])
+        trows = [c["tgt"][r * (K + 1) + j, :V] for j in range(b + 1)]
+        drows = [] if c["greedy"] else [c["drf"][r * K + j, :V] for j in range(b)]
+        oracle.verify_request(r, trows, drows, c["toks"][r], b, V, c["omode"], c["tau"],
+                              c["seed"], step)
+        rows += b + 1
+    return rows
+
+
+def cpu_baseline(args, w, tgt_full, drf_full, toks_np):
+    """The oracle on the host, before anything touches the GPU: whole steps
+    (budget, pack, verify) on one thread, then with the requests of each step
+    spread over a pool of worker processes (budget and pack stay in the
+    parent).  Returns the cpu_baseline object (the pool's figure)."""
+    import multiprocessing as mp
+
+    import oracle
+    K, V, n = w.k_max, w.vocab, w.n
+    greedy = args.mode == "greedy"
+    omode = oracle.GREEDY if greedy else oracle.STOCHASTIC
+    cost = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+
+    def budget_and_pack():
+        ob = oracle.budget_select(w.conf, w.draft_len, K, cost, w.t_base, w.n_bonus)
+        op = oracle.pack_varlen(ob["kept"], w.last_token, toks_np, K)
+        return ob["kept"], op["cu_rows"]
+
+    kept, cu = budget_and_pack()
+    # the packed target rows a varlen forward would write for this budget
+    idx = np.concatenate([r * (K + 1) + np.arange(int(kept[r]) + 1) for r in range(n)])
+    tp_h = tgt_full[idx]
+    half = args.cpu_seconds / 2
+
+    steps1, rows1 = 0, 0
+    t_c = time.perf_counter()
+    while steps1 == 0 or time.perf_counter() - t_c < half:
+        kept, cu = budget_and_pack()
+        oracle.verify(tp_h, None if greedy else drf_full, toks_np, cu, K, V, omode, w.tau,
+                      w.seed, steps1)
+        steps1 += 1
+        rows1 += int(cu[-1])
+    t1 = time.perf_counter() - t_c
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    _CPU.update(K=K, V=V, kept=kept, tgt=tgt_full, drf=drf_full, toks=toks_np, greedy=greedy,
+                omode=omode, tau=w.tau, seed=w.seed)
+    chunks = min(n, 4 * workers)
+    bounds = [n * i // chunks for i in range(chunks + 1)]
+    steps2, rows2 = 0, 0
+    with mp.get_context("fork").Pool(workers) as pool:
+        t_c = time.perf_counter()
+        while steps2 == 0 or time.perf_counter() - t_c < half:
+            kept_s, cu = budget_and_pack()
+            jobs = [(bounds[i], bounds[i + 1], steps2) for i in range(chunks)]
+            rows2 += sum(pool.map(_oracle_requests, jobs))
+            steps2 += 1
+        t2 = time.perf_counter() - t_c
+    _CPU.clear()
+    rows_step = int(cu[-1])
+    return {"value": round(rows2 / t2, 2), "unit": "rows/s", "cores": workers, "kind": "oracle",
+            "sample": f"{steps2} whole steps of {args.workload} (budget and pack in the parent, "
+                      f"{args.mode} verify of {rows_step} target rows each spread over {workers} "
+                      f"worker processes, Philox step varied) with numpy fp64, {t2:.1f} s; on one "
+                      f"thread {steps1} steps in {t1:.1f} s = {rows1 / t1:.2f} rows/s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -136,9 +218,6 @@ def main():
     import adaptive_draft_verification_amd as sv
     import workloads
 
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
     w = workloads.make(args.workload)
     mode = sv.SV_GREEDY if args.mode == "greedy" else sv.SV_STOCHASTIC
     ldt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -160,6 +239,17 @@ def main():
         w.drop_cache()
     print(f"[bench] generated {args.workload} in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
+
+    # the CPU oracle first: its worker processes fork before the GPU is touched
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, w, tgt_full, drf_full, toks_np)
+        print(f"[bench] cpu baseline: {cpu['value']} rows/s on {cpu['cores']} workers",
+              file=sys.stderr, flush=True)
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
 
     def d(a, dtype=None):
         t = torch.from_numpy(np.ascontiguousarray(a))
@@ -412,28 +502,6 @@ def main():
     budget_allocate_us = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
 
     # ------------------------------------------------------------ CPU oracle leg
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        tp_h = tgt_full[idx]
-        omode = oracle.GREEDY if mode == sv.SV_GREEDY else oracle.STOCHASTIC
-        steps_cpu, rows_cpu = 0, 0
-        t_c = time.perf_counter()
-        while steps_cpu == 0 or time.perf_counter() - t_c < args.cpu_seconds:
-            cost_o = oracle.cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
-            ob = oracle.budget_select(w.conf, w.draft_len, K, cost_o, w.t_base, w.n_bonus)
-            op = oracle.pack_varlen(ob["kept"], w.last_token, toks_np, K)
-            oracle.verify(tp_h, drf_full if mode == sv.SV_STOCHASTIC else None, toks_np,
-                          op["cu_rows"], K, V, omode, w.tau, w.seed, steps_cpu)
-            steps_cpu += 1
-            rows_cpu += int(op["cu_rows"][-1])
-        t_cpu = time.perf_counter() - t_c
-        cpu = {"value": round(rows_cpu / t_cpu, 2), "unit": "rows/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"{steps_cpu} whole steps of {args.workload} (budget, pack, {args.mode} "
-                         f"verify of {rows_t} target rows each, Philox step varied) with numpy "
-                         f"fp64 on one host thread, {t_cpu:.1f} s"}
-
     traffic = measured_traffic(args.workload, args.mode)
     out = {
         "metric": METRIC,
