@@ -540,16 +540,19 @@ struct Raw8 {
     }
 };
 
-// Weights of 8 ids: residual max(0, p - q) or (unnormalised) target mass.
+// Weights of 8 ids, both in the scale of p's own sum S_p (the draw needs
+// only their ratios): the residual S_p max(0, p - q) = max(0, p' - rq q') with
+// p' = 2^(z_p c - ap), q' = 2^(z_q c - aq) and rq = S_p / S_q, one fused
+// multiply-add and no normalising multiply; or the target mass p'.
 template <bool RESID>
 __device__ __forceinline__ void weights_from(const float* zp, const float* zq, float c, float ap,
-                                             float isp, float aq, float isq, float* w) {
+                                             float aq, float rq, float* w) {
     if (RESID) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const float p = fast_exp2(fmaf(zp[k], c, -ap)) * isp;
-            const float q = fast_exp2(fmaf(zq[k], c, -aq)) * isq;
-            w[k] = fmaxf(0.0f, p - q);
+            const float p = fast_exp2(fmaf(zp[k], c, -ap));
+            const float q = fast_exp2(fmaf(zq[k], c, -aq));
+            w[k] = fmaxf(0.0f, fmaf(-q, rq, p));
         }
     } else {
 #pragma unroll
@@ -592,7 +595,7 @@ struct DrawRow {
     const char* qrow;
     int vocab;
     bool aligned;  // both rows 16-byte aligned
-    float c, ap, isp, aq, isq;
+    float c, ap, aq, rq;
 };
 
 // A super-group's raw words for one lane: U 8-id groups of each row.
@@ -629,7 +632,7 @@ __device__ __forceinline__ float group_lane_sum(const DrawRow& d, int g, int lan
             load8<DT>(d.prow, d.vocab, e + u * kWave * 8, d.aligned, zp);
             if (RESID) load8<DT>(d.qrow, d.vocab, e + u * kWave * 8, d.aligned, zq);
         }
-        weights_from<RESID>(zp, zq, d.c, d.ap, d.isp, d.aq, d.isq, w);
+        weights_from<RESID>(zp, zq, d.c, d.ap, d.aq, d.rq, w);
         acc += sum8(w);
     }
     return acc;
@@ -648,7 +651,7 @@ __device__ __forceinline__ float group_lane_sum(const DrawRow& d, int g, int lan
 // *mass gets W; returns -2 if W is not positive.
 template <sv_dtype DT, bool RESID>
 __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, float ap,
-                        float isp, float aq, float isq, float v, DrawSmem& sm, float* mass) {
+                        float aq, float rq, float v, DrawSmem& sm, float* mass) {
     using G = Geom<DT>;
     constexpr int kGroupIds = G::kIds;
     constexpr int kGroupsPerLane = G::kGroupsPerLane;
@@ -662,9 +665,8 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
     d.aligned = ((reinterpret_cast<uintptr_t>(prow) | reinterpret_cast<uintptr_t>(qrow)) & 15) == 0;
     d.c = c;
     d.ap = ap;
-    d.isp = isp;
     d.aq = aq;
-    d.isq = isq;
+    d.rq = rq;
     const int n_groups = (vocab + kGroupIds - 1) / kGroupIds;
 
     // ---- 1. sweep
@@ -763,7 +765,7 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
                 if (e < vocab) {
                     load8<DT>(prow, vocab, e, d.aligned, zp);
                     if (RESID) load8<DT>(qrow, vocab, e, d.aligned, zq);
-                    weights_from<RESID>(zp, zq, c, ap, isp, aq, isq, wts + k8 * 8);
+                    weights_from<RESID>(zp, zq, c, ap, aq, rq, wts + k8 * 8);
                 } else {
 #pragma unroll
                     for (int k = 0; k < 8; ++k) wts[k8 * 8 + k] = 0.0f;
@@ -1008,17 +1010,18 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
         if (L < b) {
             const float tA = sm.ta[L], tS = sm.ts[L];
             const char* qrow = a.draft + ((int64_t)r * k_max + L) * a.draft_ld_bytes;
-            token = draw_row<DT, true>(prow, qrow, a.vocab, a.c, tA, 1.0f / tS, sm.qa[L],
-                                       1.0f / sm.qs[L], v, sm.draw, &mass);
+            token = draw_row<DT, true>(prow, qrow, a.vocab, a.c, tA, sm.qa[L], tS / sm.qs[L], v,
+                                       sm.draw, &mass);
+            mass /= tS;  // the residual's weights are in units of 1 / S_p
             if (token == -2) {  // zero residual mass: draw from p instead
                 float unused;
-                token = draw_row<DT, false>(prow, prow, a.vocab, a.c, tA, 1.0f, 0.0f, 1.0f, v,
-                                            sm.draw, &unused);
+                token = draw_row<DT, false>(prow, prow, a.vocab, a.c, tA, 0.0f, 1.0f, v, sm.draw,
+                                            &unused);
             }
         } else {
             float unused;
-            token = draw_row<DT, false>(prow, prow, a.vocab, a.c, sm.ba, 1.0f, 0.0f, 1.0f, v,
-                                        sm.draw, &unused);
+            token = draw_row<DT, false>(prow, prow, a.vocab, a.c, sm.ba, 0.0f, 1.0f, v, sm.draw,
+                                        &unused);
         }
     }
     if (token < 0) {  // no id carries weight: only reachable through a numeric fault
