@@ -651,7 +651,8 @@ __device__ __forceinline__ float group_lane_sum(const DrawRow& d, int g, int lan
 // *mass gets W; returns -2 if W is not positive.
 template <sv_dtype DT, bool RESID>
 __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, float ap,
-                        float aq, float rq, float v, DrawSmem& sm, float* mass) {
+                        float aq, float rq, float v, DrawSmem& sm, float* mass,
+                        bool claims_ready = false) {
     using G = Geom<DT>;
     constexpr int kGroupIds = G::kIds;
     constexpr int kGroupsPerLane = G::kGroupsPerLane;
@@ -669,9 +670,12 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
     d.rq = rq;
     const int n_groups = (vocab + kGroupIds - 1) / kGroupIds;
 
-    // ---- 1. sweep
-    if (tid == 0) sm.next = kP2Waves;
-    __syncthreads();
+    // ---- 1. sweep (claims_ready: sm.next was set before a barrier the
+    // caller has passed)
+    if (!claims_ready) {
+        if (tid == 0) sm.next = kP2Waves;
+        __syncthreads();
+    }
     {
         // super-groups [0, n_fast) lie wholly inside an aligned row: a tight
         // loop with two register buffers in turn; the rest (the row's last,
@@ -732,28 +736,26 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
             const uint64_t past = __ballot(lpos && incl > tgt);
             bool crossing = past != 0;
             const int hl = crossing ? __builtin_ctzll(past) : 63 - __builtin_clzll(pos);
-            float run = __shfl(incl - lsum, hl);  // exclusive prefix of lane hl
-            int hit = -1, lastg = -1;
-            float hit_base = 0.0f, last_base = 0.0f;
-            for (int i = 0; i < kGroupsPerLane; ++i) {
-                const int g = hl * kGroupsPerLane + i;
-                if (g >= n_groups) break;
-                const float before = run;
-                run += sm.gsum[g];
-                if (sm.gsum[g] > 0.0f) {
-                    if (crossing && hit < 0 && run > tgt) {
-                        hit = g;
-                        hit_base = before;
-                    }
-                    lastg = g;
-                    last_base = before;
-                }
-            }
-            if (hit < 0) {  // rounding: the last positive id of the lane's last positive group
+            // lane hl's super-groups, one per lane, with a wave scan: the
+            // running sum before and after each
+            const float base = __shfl(incl - lsum, hl);  // exclusive prefix of lane hl
+            const int gi = hl * kGroupsPerLane + lane;
+            const float x = (lane < kGroupsPerLane && gi < n_groups) ? sm.gsum[gi] : 0.0f;
+            const float xi = wave_incl_sum_dpp(x, lane);
+            const float up = __shfl_up(xi, 1);  // every lane takes part in the shuffle
+            const float xe = lane == 0 ? 0.0f : up;
+            const float before = base + xe;
+            const bool posg = x > 0.0f;
+            const uint64_t hitm = __ballot(crossing && posg && base + xi > tgt);
+            int hit_lane;
+            if (hitm) {
+                hit_lane = __builtin_ctzll(hitm);
+            } else {  // rounding: the last positive id of the lane's last positive group
                 crossing = false;
-                hit = lastg;
-                hit_base = last_base;
+                hit_lane = 63 - __builtin_clzll(__ballot(posg));
             }
+            const int hit = hl * kGroupsPerLane + hit_lane;
+            const float hit_base = __shfl(before, hit_lane);
             // second look: lane l takes ids [g0 + l n, g0 + (l + 1) n), n = kIdsPerLane
             const int e0 = hit * kGroupIds + lane * kIdsPerLane;
             float wts[kIdsPerLane];
@@ -837,15 +839,32 @@ struct RowMerged {
     bool fault;      // NaN or +inf somewhere, or no finite mass
 };
 
-// Merge the parts of one row in part order (deterministic).  d: the draft id
-// whose probability is wanted, or -1.  fs: the row's feature records, or null.
-template <bool GREEDY>
-__device__ RowMerged merge_parts(const PartStat* ps, int parts, int plen, int d, float c,
-                                 const FeatPart* fs = nullptr) {
+// One row's part records, loaded into registers (parts of them).
+struct RowParts {
     PartStat p[kMaxParts];
+    __device__ __forceinline__ void load(const PartStat* ps, int parts) {
 #pragma unroll
-    for (int h = 0; h < kMaxParts; ++h)
-        if (h < parts) p[h] = ps[h];
+        for (int h = 0; h < kMaxParts; ++h)
+            if (h < parts) p[h] = ps[h];
+    }
+};
+struct RowFeats {
+    FeatPart f[kMaxParts];
+    __device__ __forceinline__ void load(const FeatPart* fs, int parts) {
+#pragma unroll
+        for (int h = 0; h < kMaxParts; ++h)
+            if (h < parts) f[h] = fs[h];
+    }
+};
+
+// Merge the parts of one row in part order (deterministic).  d: the draft id
+// whose probability is wanted, or -1.  feat: also the draft-row features, from
+// the row's feature records fs.
+template <bool GREEDY>
+__device__ __forceinline__ RowMerged merge_parts(const RowParts& rp, int parts, int plen, int d,
+                                                 float c, bool feat = false,
+                                                 const RowFeats& fs = RowFeats{}) {
+    const PartStat* p = rp.p;
     RowMerged m;
     m.A = -kInf;
     m.S = 0.0f;
@@ -896,7 +915,7 @@ __device__ RowMerged merge_parts(const PartStat* ps, int parts, int plen, int d,
         m.pd = exp2f(y) / m.S;
         m.lpd = y - log2f(m.S);
     }
-    if (fs != nullptr && !m.fault) {
+    if (feat && !m.fault) {
         // entropy = log2 S - E / S with E = sum_x 2^(y_x - A) (y_x - A): each
         // part's e moved to the row's offset A (parts without mass add nothing)
         float e = 0.0f, mx = -kInf;
@@ -904,7 +923,7 @@ __device__ RowMerged merge_parts(const PartStat* ps, int parts, int plen, int d,
         for (int h = 0; h < kMaxParts; ++h) {
             if (h >= parts) break;
             if (p[h].s > 0.0f) {
-                const FeatPart f = fs[h];
+                const FeatPart f = fs.f[h];
                 e += fast_exp2(p[h].a - m.A) * fmaf(p[h].a - m.A, p[h].s, f.e);
                 mx = fmaxf(mx, f.mx);
             }
@@ -923,6 +942,7 @@ struct FinishSmem {
     int gidx[kWave];                                   // greedy: argmax of target row j
     float ba, bs;                                      // bonus row b (stochastic)
     int bidx;                                          // bonus row b (greedy)
+    float v;                                           // the draw's uniform (position L)
     int L, b, lo, fault;
 };
 
@@ -933,35 +953,39 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
     const int parts = row_parts(a.vocab), plen = part_len(a.vocab, parts);
     const PartStat* st = a.stats + (int64_t)r * (2 * k_max + 1) * kMaxParts;
     if (tid < kWave) {
-        // lane j: position j (target row j and draft row j); lane 0 also
-        // merges the bonus row b
-        const int lane = tid;
+        // lane j: position j (target row j and draft row j); lane b also
+        // merges the bonus row (target row b).  Every load this wave needs is
+        // issued before the offsets are checked: the draft id and the part
+        // records of target row j and draft row j do not depend on them.
+        const int lane = tid, j = lane;
+        const bool feat = !GREEDY && (a.out_qh != nullptr || a.out_qm != nullptr);
         const int lo = a.cu_rows[r], hi = a.cu_rows[r + 1];
+        const int d = j < k_max ? a.draft_tokens[(int64_t)r * k_max + j] : -1;
+        RowParts tp, qp;
+        RowFeats fq;
+        if (j <= k_max) tp.load(st + (int64_t)j * kMaxParts, parts);
+        if (!GREEDY && j < k_max) qp.load(st + (int64_t)(k_max + 1 + j) * kMaxParts, parts);
+        if (feat && j < k_max) fq.load(a.feat + ((int64_t)r * k_max + j) * kMaxParts, parts);
+        float u = 0.0f, v = 0.0f;
+        if (!GREEDY) draw_uniforms(a.seed, a.step, (uint32_t)r, (uint32_t)j, &u, &v);
         const int b = hi - lo - 1;
         int fault = 0;
         bool acc = true;
         if (lo < 0 || b < 0 || b > k_max || (int64_t)hi > a.target_rows) {
             fault = SV_DEV_BAD_CU_ROWS;
         } else {
-            const int j = lane;
             if (j < b) {
-                const int d = a.draft_tokens[(int64_t)r * k_max + j];
                 const bool d_ok = d >= 0 && d < a.vocab;
                 if (!d_ok) fault |= SV_DEV_BAD_TOKEN;
-                const RowMerged t = merge_parts<GREEDY>(st + (int64_t)j * kMaxParts, parts,
-                                                        plen, d_ok ? d : -1, a.c);
+                const RowMerged t = merge_parts<GREEDY>(tp, parts, plen, d_ok ? d : -1, a.c);
                 if (t.fault) fault |= SV_DEV_NONFINITE;
                 if (GREEDY) {
                     acc = t.idx == d;
                     sm.gidx[j] = t.idx;
                 } else {
-                    const bool feat = a.out_qh != nullptr || a.out_qm != nullptr;
-                    const RowMerged q = merge_parts<false>(
-                        st + (int64_t)(k_max + 1 + j) * kMaxParts, parts, plen, d_ok ? d : -1,
-                        a.c, feat ? a.feat + ((int64_t)r * k_max + j) * kMaxParts : nullptr);
+                    const RowMerged q =
+                        merge_parts<false>(qp, parts, plen, d_ok ? d : -1, a.c, feat, fq);
                     if (q.fault) fault |= SV_DEV_NONFINITE;
-                    float u, v;
-                    draw_uniforms(a.seed, a.step, (uint32_t)r, (uint32_t)j, &u, &v);
                     // u < min(1, p/q), the ratio taken from log2 p - log2 q so that
                     // probabilities below fp32's normal range do not decide it
                     acc = u < exp2f(t.lpd - q.lpd);
@@ -975,9 +999,12 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
                     sm.qm[j] = q.pmax;
                 }
             }
-            if (lane == 0) {
-                const RowMerged t = merge_parts<GREEDY>(st + (int64_t)b * kMaxParts, parts,
-                                                        plen, -1, a.c);
+            // the bonus row b: lane b's own target records (a wave has 64
+            // lanes, so b = 64 is loaded here by lane 0)
+            const bool bonus_lane = b < kWave ? j == b : j == 0;
+            if (bonus_lane) {
+                if (b >= kWave) tp.load(st + (int64_t)b * kMaxParts, parts);
+                const RowMerged t = merge_parts<GREEDY>(tp, parts, plen, -1, a.c);
                 if (t.fault) fault |= SV_DEV_NONFINITE;
                 sm.ba = t.A;
                 sm.bs = t.S;
@@ -986,11 +1013,14 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
         }
         fault = wave_or_int(fault);
         const uint64_t rej = __ballot(!acc);
+        const int L = rej ? __builtin_ctzll(rej) : b;
+        if (!GREEDY && j == L) sm.v = v;  // L = 64 (every draft of 64 kept) draws it below
         if (lane == 0) {
-            sm.L = rej ? __builtin_ctzll(rej) : b;
+            sm.L = L;
             sm.b = b;
             sm.lo = lo;
             sm.fault = fault;
+            if (!GREEDY) sm.draw.next = kP2Waves;  // the draw's first claims are implicit
         }
     }
     __syncthreads();
@@ -1004,14 +1034,17 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
     if (GREEDY) {
         token = L < b ? sm.gidx[L] : sm.bidx;
     } else {
-        float u, v;
-        draw_uniforms(a.seed, a.step, (uint32_t)r, (uint32_t)L, &u, &v);
+        float v = sm.v;
+        if (L >= kWave) {
+            float u;
+            draw_uniforms(a.seed, a.step, (uint32_t)r, (uint32_t)L, &u, &v);
+        }
         const char* prow = a.target + ((int64_t)lo + L) * a.target_ld_bytes;
         if (L < b) {
             const float tA = sm.ta[L], tS = sm.ts[L];
             const char* qrow = a.draft + ((int64_t)r * k_max + L) * a.draft_ld_bytes;
             token = draw_row<DT, true>(prow, qrow, a.vocab, a.c, tA, sm.qa[L], tS / sm.qs[L], v,
-                                       sm.draw, &mass);
+                                       sm.draw, &mass, true);
             mass /= tS;  // the residual's weights are in units of 1 / S_p
             if (token == -2) {  // zero residual mass: draw from p instead
                 float unused;
@@ -1021,7 +1054,7 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
         } else {
             float unused;
             token = draw_row<DT, false>(prow, prow, a.vocab, a.c, sm.ba, 0.0f, 1.0f, v, sm.draw,
-                                        &unused);
+                                        &unused, true);
         }
     }
     if (token < 0) {  // no id carries weight: only reachable through a numeric fault
