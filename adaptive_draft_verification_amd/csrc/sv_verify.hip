@@ -31,7 +31,7 @@
 // uniforms of the kept positions, tests u < 2^(log2 p(d) - log2 q(d)) (greedy:
 // d == argmax) and takes the first rejection with a ballot.  The token at L
 // is drawn by inverse CDF over the residual row (or the bonus row): waves
-// claim 1024-id super-groups from an LDS counter and stream them (the next
+// claim 512-id super-groups from an LDS counter and stream them (the next
 // one's loads in flight while the current one is summed, no barrier in the
 // stream), each super-group's sum goes to LDS, and wave 0 walks the sums in
 // id order and reads only the crossing super-group again.
@@ -46,8 +46,9 @@ namespace {
 // the stream from ~5.8 to ~6.5 TB/s; 512-thread workgroups beat 256 and 1024;
 // with the dense order, parts of up to 131072 ids (one per row here) beat
 // 65536 (74.7 vs 76.8 us) and smaller parts lose more (3 parts 81, 4 parts
-// 88 us); an unroll of 8 loses to 4; draw super-groups of 2 x 512 ids per
-// wave beat 4 x 512 (35 vs 37 us).
+// 88 us); an unroll of 8 loses to 4; bf16 draw super-groups of 512 ids per
+// wave beat 1024 (28.4 vs 29.1 us: finer claims even out the waves' ends and
+// the second look is shorter), 1536 (30.4) and 2048 (35.2).
 #ifndef SV_PASS1_THREADS
 #define SV_PASS1_THREADS 512
 #endif
@@ -58,7 +59,7 @@ namespace {
 #define SV_PASS1_NONTEMPORAL 1
 #endif
 #ifndef SV_DRAW_UNROLL
-#define SV_DRAW_UNROLL 2
+#define SV_DRAW_UNROLL 1
 #endif
 constexpr int kThreads = SV_PASS1_THREADS;           // pass 1 workgroup
 constexpr int kUnroll = SV_PASS1_UNROLL;             // pass 1: 16-byte loads in flight per thread
