@@ -188,6 +188,17 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
     }
 }
 
+// The per-wave totals tot[0 .. kWaves) in LDS: the sum over the waves before
+// `wave`, and (*all) over every wave.  Lane v reads tot[v] once and a DPP wave
+// scan does the rest, instead of a chain of dependent LDS reads.
+template <typename T>
+__device__ __forceinline__ T waves_before(const T* tot, int wave, int lane, T* all) {
+    const T x = lane < kWaves ? tot[lane] : T(0);
+    const T incl = wave_incl_sum_dpp<T>(x, lane);
+    *all = lane63(incl);
+    return __shfl(incl - x, wave);
+}
+
 // (score, B) pair; the better one has the larger score, then the smaller B.
 struct Cand {
     double score;
@@ -201,27 +212,41 @@ struct BetterOp {
     }
 };
 
-// kept[r] = #{j : rank(r, j) < B}.  rk[q] holds the rank of slot
-// tid + 1024 q (slots past draft_len rank at `total` or later, never before
-// B <= total).  kept_s (LDS, or null) gets a copy.  Every thread of the
-// workgroup calls this (one barrier).
-__device__ __forceinline__ void write_kept(const int32_t* rk, int per, int B, int n_req,
-                                           int k_max, uint8_t* in_budget,
-                                           int32_t* __restrict__ kept, uint8_t* kept_s) {
+// kept[r] = #{j : rank(r, j) < B}.  A request's real slots rank in position
+// order (survival never rises along a chain, ties go to the lower slot) and
+// its slots past draft_len rank at `total` or later, never before B <= total,
+// so the kept slots are a prefix: the request's count is written by the slot
+// that ends it (in budget, its successor not), or by slot 0 when slot 0 is
+// not in budget.  rk[q], rk1[q]: the ranks of slot tid + 1024 q and of the
+// slot after it.  kept_s (LDS, or null) gets a copy; no barrier inside.
+__device__ __forceinline__ void write_kept(const int32_t* rk, const int32_t* rk1, int per, int B,
+                                           int n_req, int k_max, int32_t* __restrict__ kept,
+                                           uint8_t* kept_s) {
     const int tid = threadIdx.x;
     const int n_slots = n_req * k_max;
+    if (k_max == 0) {
+        for (int r = tid; r < n_req; r += kThreads) {
+            kept[r] = 0;
+            if (kept_s != nullptr) kept_s[r] = 0;
+        }
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
         if (q >= per) break;  // uniform
         const int x = tid + q * kThreads;
-        if (x < n_slots) in_budget[x] = rk[q] < B ? 1 : 0;
-    }
-    __syncthreads();
-    for (int r = tid; r < n_req; r += kThreads) {
-        int k_in = 0;
-        for (int j = 0; j < k_max; ++j) k_in += in_budget[r * k_max + j];
-        kept[r] = k_in;
-        if (kept_s != nullptr) kept_s[r] = (uint8_t)k_in;
+        if (x < n_slots) {
+            const int r = x / k_max, j = x - r * k_max;
+            const bool in = rk[q] < B;
+            const bool next_in = j + 1 < k_max && rk1[q] < B;
+            int k_in = -1;
+            if (j == 0 && !in) k_in = 0;
+            if (in && !next_in) k_in = j + 1;
+            if (k_in >= 0) {
+                kept[r] = k_in;
+                if (kept_s != nullptr) kept_s[r] = (uint8_t)k_in;
+            }
+        }
     }
 }
 
@@ -273,8 +298,8 @@ __device__ void pack_from_lds(const uint8_t* kept_s, int n_req, int k_max, const
     const int incl = wave_incl_sum_dpp(local, lane);
     if (lane == kWave - 1) wave_tot[wave] = incl;
     __syncthreads();
-    int start = incl - local;
-    for (int v = 0; v < wave; ++v) start += wave_tot[v];
+    int total = 0;
+    int start = incl - local + waves_before(wave_tot, wave, lane, &total);
     for (int i = 0; i < per; ++i) {
         const int r = first + i;
         if (r < n_req) {
@@ -283,8 +308,6 @@ __device__ void pack_from_lds(const uint8_t* kept_s, int n_req, int k_max, const
             start += (int)kept_s[r] + 1;
         }
     }
-    int total = 0;
-    for (int v = 0; v < kWaves; ++v) total += wave_tot[v];
     if (tid == 0) po.cu_rows[n_req] = total;
     __syncthreads();
     // row 0 of each request: its last token; row 1 + j: draft j, if kept
@@ -321,13 +344,11 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     int n_req, int k_max, const float* __restrict__ cost, int t_base, int n_bonus,
     int32_t* __restrict__ kept, int32_t* __restrict__ budget, int32_t* dev_error, void* ws,
     PackOut po) {
-    __shared__ uint8_t in_budget[SV_MAX_BUDGET_SLOTS];
     __shared__ uint8_t kept_s[PACK ? SV_MAX_BUDGET_SLOTS : 1];
     __shared__ int32_t cu_s[PACK ? SV_MAX_BUDGET_SLOTS : 1];
     __shared__ int32_t pack_tot[kWaves];
     __shared__ uint64_t wave_tot[kWaves];
     __shared__ Cand wave_best[kWaves];
-    __shared__ int32_t best_b_s;
     __shared__ int32_t err_s;
 
     const int tid = threadIdx.x;
@@ -340,14 +361,16 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     const int first = tid * per;
 
     // every load first: rank-ordered survivals and cost entries of this
-    // thread's ranks, the ranks of slots tid + 1024 q, the total
+    // thread's ranks, the ranks of slots tid + 1024 q and of their successors,
+    // the total
     float srt[kPerThread], cst[kPerThread];
-    int32_t rk[kPerThread];
+    int32_t rk[kPerThread], rk1[kPerThread];
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
         srt[q] = 0.0f;
         cst[q] = 1.0f;
         rk[q] = 0;
+        rk1[q] = 0;
         if (q >= per) continue;  // uniform: per = ceil(n_slots / 1024)
         const int rank = first + q;
         if (rank < n_slots) {
@@ -356,6 +379,7 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
         }
         const int x = tid + q * kThreads;
         if (x < n_slots) rk[q] = w.rank[x];
+        if (x + 1 < n_slots) rk1[q] = w.rank[x + 1];
     }
     const float cost0 = cost[t_base];
     const int total = n_slots > 0 ? w.total[0] : 0;
@@ -375,8 +399,9 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     const uint64_t incl = wave_incl_sum_dpp<uint64_t>(local, lane);
     if (lane == kWave - 1) wave_tot[wave] = incl;
     __syncthreads();
-    uint64_t run_sum = incl - local;
-    for (int v = 0; v < wave; ++v) run_sum += wave_tot[v];
+    uint64_t all_waves;  // unused here
+    uint64_t run_sum = incl - local + waves_before(wave_tot, wave, lane, &all_waves);
+    (void)all_waves;
 
     Cand best{-__builtin_inf(), 0x7fffffff, 0};
     int cost_err = 0;
@@ -406,14 +431,10 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     if (cost_err) atomicOr(&err_s, cost_err);
     if (lane == 0) wave_best[wave] = best;
     __syncthreads();
-    if (wave == 0) {
-        Cand c = lane < kWaves ? wave_best[lane] : Cand{-__builtin_inf(), 0x7fffffff, 0};
-        c = lane63(wave_scan_dpp(c, lane, BetterOp{}));
-        if (lane == 0) best_b_s = c.b;
-    }
-    __syncthreads();
-    const int B = best_b_s;
-    write_kept(rk, per, B, n_req, k_max, in_budget, kept, PACK ? kept_s : nullptr);
+    // every wave reduces the 16 wave winners itself: no further barrier
+    Cand c = lane < kWaves ? wave_best[lane] : Cand{-__builtin_inf(), 0x7fffffff, 0};
+    const int B = lane63(wave_scan_dpp(c, lane, BetterOp{})).b;
+    write_kept(rk, rk1, per, B, n_req, k_max, kept, PACK ? kept_s : nullptr);
     if (tid == 0) {
         budget[0] = B;
         raise_error(dev_error, err_s);
@@ -434,7 +455,6 @@ __global__ __launch_bounds__(kThreads) void allocate_kernel(int n_req, int k_max
                                                             int32_t* __restrict__ kept,
                                                             int32_t* budget_used, void* ws,
                                                             PackOut po) {
-    __shared__ uint8_t in_budget[SV_MAX_BUDGET_SLOTS];
     __shared__ uint8_t kept_s[PACK ? SV_MAX_BUDGET_SLOTS : 1];
     __shared__ int32_t cu_s[PACK ? SV_MAX_BUDGET_SLOTS : 1];
     __shared__ int32_t pack_tot[kWaves];
@@ -444,18 +464,20 @@ __global__ __launch_bounds__(kThreads) void allocate_kernel(int n_req, int k_max
     const int n_slots = n_req * k_max;
     const BudgetWs w = budget_ws(ws, n_slots);
     const int per = (n_slots + kThreads - 1) / kThreads;
-    int32_t rk[kPerThread];
+    int32_t rk[kPerThread], rk1[kPerThread];
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
         rk[q] = 0;
+        rk1[q] = 0;
         if (q >= per) continue;  // uniform
         const int x = tid + q * kThreads;
         if (x < n_slots) rk[q] = w.rank[x];
+        if (x + 1 < n_slots) rk1[q] = w.rank[x + 1];
     }
     const int total = n_slots > 0 ? w.total[0] : 0;
     const int b_in = budget_in[0];
     const int B = b_in < 0 ? 0 : (b_in > total ? total : b_in);
-    write_kept(rk, per, B, n_req, k_max, in_budget, kept, PACK ? kept_s : nullptr);
+    write_kept(rk, rk1, per, B, n_req, k_max, kept, PACK ? kept_s : nullptr);
     if (tid == 0 && budget_used != nullptr) budget_used[0] = B;
     if (PACK) {
         __syncthreads();

@@ -61,9 +61,19 @@ def logits_dtype(w):
 # ------------------------------------------------------------------ budget
 
 def gpu_budget(conf, draft_len, cost, t_base, n_bonus):
-    out = sv.budget_select(to_dev(np.asarray(conf, np.float32)),
-                           to_dev(np.asarray(draft_len, np.int32)),
-                           to_dev(np.asarray(cost, np.float32)), t_base, n_bonus)
+    """sv_budget_select with every output pre-filled with a sentinel (-7, NaN), so
+    that a value the kernels fail to write cannot pass on stale memory."""
+    conf = np.asarray(conf, np.float32)
+    n, k = conf.shape
+    out = dict(kept=torch.full((n,), -7, dtype=torch.int32, device="cuda"),
+               budget=torch.full((1,), -7, dtype=torch.int32, device="cuda"),
+               survival=torch.full((n, k), float("nan"), dtype=torch.float32, device="cuda"),
+               dev_error=torch.zeros(1, dtype=torch.int32, device="cuda"))
+    ws = torch.empty(max(1, sv.sv_budget_workspace_bytes(n, k)), dtype=torch.uint8,
+                     device="cuda")
+    sv.sv_budget_select(to_dev(conf), to_dev(np.asarray(draft_len, np.int32)),
+                        to_dev(np.asarray(cost, np.float32)), t_base, n_bonus, out["kept"],
+                        out["budget"], out["survival"], out["dev_error"], ws=ws)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -81,8 +91,16 @@ def check_budget(conf, draft_len, k_max, cost, t_base, n_bonus):
 def check_allocate(conf, draft_len, k_max, budget):
     """Allocation of a given budget: kept counts, the clamped B, survival bits."""
     conf = np.asarray(conf, np.float32).reshape(len(draft_len), k_max)
-    g = sv.budget_allocate(to_dev(conf), to_dev(np.asarray(draft_len, np.int32)),
-                           to_dev(np.array([budget], np.int32)))
+    n = len(draft_len)
+    g = dict(kept=torch.full((n,), -7, dtype=torch.int32, device="cuda"),
+             budget_used=torch.full((1,), -7, dtype=torch.int32, device="cuda"),
+             survival=torch.full((n, k_max), float("nan"), dtype=torch.float32, device="cuda"),
+             dev_error=torch.zeros(1, dtype=torch.int32, device="cuda"))
+    ws = torch.empty(max(1, sv.sv_budget_workspace_bytes(n, k_max)), dtype=torch.uint8,
+                     device="cuda")
+    sv.sv_budget_allocate(to_dev(conf), to_dev(np.asarray(draft_len, np.int32)),
+                          to_dev(np.array([budget], np.int32)), g["kept"], g["budget_used"],
+                          g["survival"], g["dev_error"], ws=ws)
     torch.cuda.synchronize()
     o = oracle.budget_allocate(conf, draft_len, k_max, budget)
     np.testing.assert_array_equal(g["kept"].cpu().numpy(), o["kept"])
