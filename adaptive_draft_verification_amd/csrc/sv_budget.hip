@@ -136,8 +136,13 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
         }
     }
     if (lead) {
-        if (my_total) atomicAdd(&total_s, my_total);
-        if (my_err) atomicOr(&err_s, my_err);
+        // one LDS atomic per wave (contended per-thread LDS atomics serialise)
+        my_total = wave_sum_dpp(my_total, lane);
+        my_err = wave_or_int(my_err);
+        if (lane == 0) {
+            if (my_total) atomicAdd(&total_s, my_total);
+            if (my_err) atomicOr(&err_s, my_err);
+        }
     }
     __syncthreads();
     if (lead) {
@@ -488,23 +493,27 @@ __global__ __launch_bounds__(kThreads) void allocate_kernel(int n_req, int k_max
 // One draft length for the whole batch ("Hardware-Aware Dynamic Speculative
 // Decoding (DSD), feat. Cohere", section "동적 추측 디코딩(DSD)의 핵심
 // 아이디어": K chosen by goodput = acceptance length / step latency).  One
-// workgroup: confidences staged in LDS, one thread per request forms its
-// survival chain and adds floor(s * 2^40) of position j into column j (LDS
-// integer atomics: exact, order free); thread K forms
-// S(K) = sum of columns j < K and T(K) = drafts verified at K, and the score
-// (n_bonus + S * 2^-40) / cost[t_base + T] in IEEE fp64; the first maximiser
-// is K*, and kept[r] = min(K*, K_r).
+// workgroup: confidences staged in LDS; one thread per request forms its
+// survival chain, stores floor(s * 2^40) of position j at column j of an LDS
+// table (0 past draft_len) and counts its clamped draft length in a small
+// histogram; wave w then sums columns w, w + 16, ... (a DPP wave sum of
+// exact uint64 fixed-point values: order free, no contended atomics).
+// Thread K forms S(K) = sum of columns j < K and T(K) = drafts verified at K
+// (from the histogram), and the score (n_bonus + S * 2^-40) / cost[t_base + T]
+// in IEEE fp64; the first maximiser is K*, and kept[r] = min(K*, K_r).
 __global__ __launch_bounds__(kThreads) void uniform_k_kernel(
     const float* __restrict__ conf, const int32_t* __restrict__ draft_len, int n_req, int k_max,
     const float* __restrict__ cost, int t_base, int n_bonus, int32_t* __restrict__ kept,
     int32_t* __restrict__ k_out, double* __restrict__ scores, int32_t* dev_error) {
     __shared__ float conf_s[kConfLds];
+    __shared__ uint64_t fx_s[SV_MAX_BUDGET_SLOTS];  // column j at j * n_req
     __shared__ unsigned long long col_sum[SV_MAX_DRAFT];
-    __shared__ int32_t col_cnt[SV_MAX_DRAFT];
+    __shared__ int32_t len_hist[SV_MAX_DRAFT + 1];
     __shared__ double score_s[SV_MAX_DRAFT + 1];
     __shared__ int32_t err_s, best_s;
 
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
     const int n_slots = n_req * k_max;
     const int kp = k_max | 1;
     float c[kPerThread];
@@ -515,10 +524,7 @@ __global__ __launch_bounds__(kThreads) void uniform_k_kernel(
         c[q] = x < n_slots ? conf[x] : 0.0f;
         dl[q] = x < n_req ? draft_len[x] : 0;
     }
-    if (tid < SV_MAX_DRAFT) {
-        col_sum[tid] = 0ull;
-        col_cnt[tid] = 0;
-    }
+    if (tid <= SV_MAX_DRAFT) len_hist[tid] = 0;
     if (tid == 0) err_s = 0;
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
@@ -537,26 +543,51 @@ __global__ __launch_bounds__(kThreads) void uniform_k_kernel(
         if (r < n_req) {
             const int K = clamp_len(dl[q], k_max);
             if (K != dl[q]) my_err |= SV_DEV_BAD_DRAFT_LEN;
+
             float sv = 1.0f;
-            for (int j = 0; j < K; ++j) {
-                sv = __fmul_rn(sv, conf_s[r * kp + j]);
-                // s * 2^40 is exact in fp32; the conversion truncates = floor
-                atomicAdd(&col_sum[j], (unsigned long long)(sv * 0x1p40f));
-                atomicAdd(&col_cnt[j], 1);
+            for (int j = 0; j < k_max; ++j) {
+                uint64_t f = 0;
+                if (j < K) {
+                    sv = __fmul_rn(sv, conf_s[r * kp + j]);
+                    // s * 2^40 is exact in fp32; the conversion truncates = floor
+                    f = (uint64_t)(sv * 0x1p40f);
+                }
+                fx_s[j * n_req + r] = f;
             }
         }
     }
-    if (my_err) atomicOr(&err_s, my_err);
+    // the histogram of clamped draft lengths: a ballot per length counts a
+    // wave's requests at once (one LDS add per wave and length)
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int base = tid - lane + q * kThreads;
+        if (base >= n_req) break;  // uniform
+        const int r = base + lane;
+        const int K = r < n_req ? clamp_len(dl[q], k_max) : -1;
+        for (int len = 0; len <= k_max; ++len) {
+            const uint64_t m = __ballot(K == len);
+            if (lane == 0 && m) atomicAdd(&len_hist[len], (int)__popcll(m));
+        }
+    }
+    my_err = wave_or_int(my_err);
+    if (lane == 0 && my_err) atomicOr(&err_s, my_err);
+    __syncthreads();
+
+    for (int j = wave; j < k_max; j += kWaves) {
+        uint64_t part = 0;
+        for (int r = lane; r < n_req; r += kWave) part += fx_s[j * n_req + r];
+        part = wave_sum_dpp(part, lane);
+        if (lane == 0) col_sum[j] = part;
+    }
     __syncthreads();
 
     if (tid <= k_max) {
         const int K = tid;
         unsigned long long S = 0ull;
         int T = 0;
-        for (int j = 0; j < K; ++j) {
-            S += col_sum[j];
-            T += col_cnt[j];
-        }
+        for (int j = 0; j < K; ++j) S += col_sum[j];
+        // drafts verified at K: sum over requests of min(K, K_r)
+        for (int len = 1; len <= k_max; ++len) T += len_hist[len] * (len < K ? len : K);
         const float cst = cost[t_base + T];
         double sc = -__builtin_inf();
         if (cst > 0.0f && is_finite_bits(cst)) {

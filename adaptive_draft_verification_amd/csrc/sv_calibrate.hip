@@ -58,19 +58,6 @@ __device__ __forceinline__ float logit(const float* th, int j, int k_max, const 
 
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-// Block-wide sum of one float per thread in a fixed order (DPP within each
-// wave, then the wave totals in wave order).  Every thread gets the sum.
-__device__ float block_sum(float v, float* red) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const float w = wave_sum_dpp(v, lane);
-    if (lane == 0) red[wave] = w;
-    __syncthreads();
-    float t = red[0];
-    for (int i = 1; i < kWaves; ++i) t += red[i];
-    __syncthreads();
-    return t;
-}
-
 __global__ __launch_bounds__(kThreads) void accept_stats_kernel(
     const int32_t* __restrict__ accepted, const int32_t* __restrict__ cu_rows, int n_req,
     int k_max, unsigned long long* attempted, unsigned long long* accepted_at,
@@ -78,6 +65,7 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(
     __shared__ unsigned int att_s[SV_MAX_DRAFT], acc_s[SV_MAX_DRAFT];
     __shared__ unsigned long long req_s, emit_s;
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
     if (tid < SV_MAX_DRAFT) {
         att_s[tid] = 0u;
         acc_s[tid] = 0u;
@@ -88,19 +76,34 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(
     }
     __syncthreads();
     unsigned long long my_req = 0, my_emit = 0;
-    for (int r = tid; r < n_req; r += kThreads) {
-        int b, L;
-        if (!outcome(accepted, cu_rows, r, k_max, &b, &L)) continue;
-        ++my_req;
-        my_emit += (unsigned long long)(L + 1);
-        const int last = L < b - 1 ? L : b - 1;  // verified positions 0 .. last
-        for (int j = 0; j <= last; ++j) {
-            atomicAdd(&att_s[j], 1u);
-            if (j < L) atomicAdd(&acc_s[j], 1u);
+    // whole waves step through the requests together, so that a ballot per
+    // position counts a wave's 64 requests at once (one LDS add per wave)
+    for (int base = tid - lane; base < n_req; base += kThreads) {
+        const int r = base + lane;
+        int b = 0, L = -1;
+        const bool ok = r < n_req && outcome(accepted, cu_rows, r, k_max, &b, &L);
+        const int last = !ok ? -1 : (L < b - 1 ? L : b - 1);  // verified positions 0 .. last
+        if (ok) {
+            ++my_req;
+            my_emit += (unsigned long long)(L + 1);
+        }
+        for (int j = 0; j < k_max; ++j) {
+            const uint64_t ver = __ballot(j <= last);
+            if (ver == 0) break;  // positions only shrink from here (uniform)
+            const uint64_t acc = __ballot(j <= last && j < L);
+            if (lane == 0) {
+                atomicAdd(&att_s[j], (unsigned int)__popcll(ver));
+                if (acc) atomicAdd(&acc_s[j], (unsigned int)__popcll(acc));
+            }
         }
     }
-    if (my_req) atomicAdd(&req_s, my_req);
-    if (my_emit) atomicAdd(&emit_s, my_emit);
+    // one LDS add per wave for the totals as well
+    my_req = wave_sum_dpp(my_req, lane);
+    my_emit = wave_sum_dpp(my_emit, lane);
+    if (lane == 0 && my_req) {
+        atomicAdd(&req_s, my_req);
+        atomicAdd(&emit_s, my_emit);
+    }
     __syncthreads();
     if (tid < k_max) {
         if (att_s[tid]) atomicAdd(&attempted[tid], (unsigned long long)att_s[tid]);
@@ -113,28 +116,31 @@ __global__ __launch_bounds__(kThreads) void accept_stats_kernel(
 }
 
 // One gradient step on the mean log-loss of the verified positions:
-// theta <- theta - lr * grad / N.  One workgroup; each gradient component is
-// a fixed-order block sum (deterministic).
+// theta <- theta - lr * grad / N.  One workgroup, one pass: wave w takes the
+// positions j = w, w + 16, ...; its lanes walk the requests r = lane,
+// lane + 64, ... in order, so each alpha component is a fixed-order sum (the
+// lanes' partial sums, then a DPP wave sum) and each beta component the waves'
+// sums added in wave order: deterministic, with no barrier per position.
 __global__ __launch_bounds__(kThreads) void calibrate_update_kernel(
     float* theta, Features f, const int32_t* __restrict__ accepted,
     const int32_t* __restrict__ cu_rows, int n_req, int k_max, float lr, int32_t* count_out) {
     __shared__ float th[SV_MAX_DRAFT + kFeat];
-    __shared__ float red[kWaves];
     __shared__ float grad[SV_MAX_DRAFT + kFeat];
+    __shared__ float beta_w[kWaves][kFeat];
     __shared__ int cnt_s;
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
     if (tid < k_max + kFeat) th[tid] = theta[tid];
     if (tid == 0) cnt_s = 0;
     __syncthreads();
     float g_beta[kFeat] = {0.0f, 0.0f, 0.0f};
     int my_cnt = 0;
-    for (int j = 0; j < k_max; ++j) {
-        // this thread's requests, in order, that verified position j
+    for (int j = wave; j < k_max; j += kWaves) {
         float g = 0.0f;
-        for (int r = tid; r < n_req; r += kThreads) {
+        for (int r = lane; r < n_req; r += kWave) {
             int b, L;
             if (!outcome(accepted, cu_rows, r, k_max, &b, &L)) continue;
-            if (j > L || j >= b) continue;
+            if (j > L || j >= b) continue;  // position j not verified for r
             float x[kFeat];
             features(f, (int64_t)r * k_max + j, x);
             const float err = sigmoid(logit(th, j, k_max, x)) - (j < L ? 1.0f : 0.0f);
@@ -143,15 +149,22 @@ __global__ __launch_bounds__(kThreads) void calibrate_update_kernel(
             for (int i = 0; i < kFeat; ++i) g_beta[i] += err * x[i];
             ++my_cnt;
         }
-        g = block_sum(g, red);
-        if (tid == 0) grad[j] = g;
+        g = wave_sum_dpp(g, lane);
+        if (lane == 0) grad[j] = g;
     }
 #pragma unroll
     for (int i = 0; i < kFeat; ++i) {
-        const float g = block_sum(g_beta[i], red);
-        if (tid == 0) grad[k_max + i] = g;
+        const float gw = wave_sum_dpp(g_beta[i], lane);
+        if (lane == 0) beta_w[wave][i] = gw;
     }
-    if (my_cnt) atomicAdd(&cnt_s, my_cnt);
+    my_cnt = wave_sum_dpp(my_cnt, lane);  // one LDS add per wave
+    if (lane == 0 && my_cnt) atomicAdd(&cnt_s, my_cnt);
+    __syncthreads();
+    if (tid < kFeat) {
+        float t = beta_w[0][tid];
+        for (int w = 1; w < kWaves; ++w) t += beta_w[w][tid];
+        grad[k_max + tid] = t;
+    }
     __syncthreads();
     const int count = cnt_s;
     if (tid < k_max + kFeat && count > 0) theta[tid] = th[tid] - lr * (grad[tid] / (float)count);

@@ -26,8 +26,10 @@ rows each draw reads again) are reported beside it.  A second leg verifies
 every draft (full K: 2048 target + 1792 draft rows) for the bandwidth figure
 at the largest size.  Two smaller legs time pass 1 with the draft-row
 features (entropy, largest probability) accumulated as well, and the one-K-
-per-batch selection (sv_uniform_k_select), and the allocation of a budget
-sized one step ahead (sv_budget_allocate).  Before the GPU is touched, the CPU
+per-batch selection (sv_uniform_k_select), the allocation of a budget
+sized one step ahead (sv_budget_allocate), and the acceptance counters and
+the logistic calibration's update and prediction fed by one verify step
+(sv_accept_stats, sv_calibrate_update, sv_calibrate_predict).  Before the GPU is touched, the CPU
 oracle runs whole steps of the same workload on the host for the cpu_baseline
 figure: half the time on one thread, half with each step's requests spread
 over a pool of worker processes (the reported value; the one-thread rate is in
@@ -422,6 +424,33 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / iters
 
+    def graph_us(fn, iters):
+        """GPU time per call of a small entry point: `iters` calls captured in one
+        HIP graph and replayed between two events, so the figure is the kernels'
+        own time back to back, not the host's per-call binding overhead (which
+        exceeds these kernels' few microseconds when they are launched from
+        Python one by one)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(iters):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(cur)
+        g.replay()
+        b_.record(cur)
+        torch.cuda.synchronize()
+        return round(a_.elapsed_time(b_) / iters * 1e3, 2)
+
     ms_per_step = wall * 1e3 / args.steps
     pass1_ms, pass2_ms = float(np.mean(stage_ms[:, 2])), float(np.mean(stage_ms[:, 3]))
     roof_ms = pass1_launch_ms(args.steps)
@@ -475,31 +504,42 @@ def main():
     # the DSD-style alternative to the adaptive budget: one K for the batch
     uk_k = torch.empty(1, dtype=torch.int32, device=dev)
     uk_kept = torch.empty(n, dtype=torch.int32, device=dev)
-    for _ in range(3):
-        sv.sv_uniform_k_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, uk_kept, uk_k, None,
-                               err)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        sv.sv_uniform_k_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, uk_kept, uk_k, None,
-                               err)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    uniform_k = {"us": round(e0.elapsed_time(e1) / args.steps * 1e3, 2), "k": int(uk_k.item()),
-                 "drafts_verified": int(uk_kept.sum().item())}
+    uk_us = graph_us(lambda: sv.sv_uniform_k_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus,
+                                                    uk_kept, uk_k, None, err), args.steps)
+    uniform_k = {"us": uk_us, "k": int(uk_k.item()), "drafts_verified": int(uk_kept.sum().item())}
 
     # ----------------------------------------- stale-confidence budget leg
     # the pipeline that sizes B one step ahead: the step itself only allocates
     # the slots of a B already in device memory (here the budget selected above)
     al_kept = torch.empty(n, dtype=torch.int32, device=dev)
-    for _ in range(3):
-        sv.sv_budget_allocate(conf_d, dl_d, budget, al_kept, None, None, err, ws=bws)
-    e0.record(stream)
-    for _ in range(args.steps):
-        sv.sv_budget_allocate(conf_d, dl_d, budget, al_kept, None, None, err, ws=bws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    budget_allocate_us = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
+    budget_allocate_us = graph_us(
+        lambda: sv.sv_budget_allocate(conf_d, dl_d, budget, al_kept, None, None, err, ws=bws),
+        args.steps)
+
+    # ------------------------------------------ acceptance statistics and calibration leg
+    # one verify with the draft-row features, then the per-position counters and
+    # one update and prediction of the logistic acceptance model from its outcome
+    calibration = None
+    if mode == sv.SV_STOCHASTIC:
+        qh = torch.empty(n, K, dtype=torch.float32, device=dev)
+        qm = torch.empty(n, K, dtype=torch.float32, device=dev)
+        tp0, dr0 = replicas[0]
+        sv.sv_verify_stages(tp0, dr0, toks_d, cu, mode, w.tau, w.seed, 0, tok_out, acc_out, ws, 3,
+                            p_out, q_out, res_out, err, vocab=V, out_q_entropy=qh, out_q_max=qm)
+        attempted = torch.zeros(K, dtype=torch.int64, device=dev)
+        accepted_at = torch.zeros(K, dtype=torch.int64, device=dev)
+        totals = torch.zeros(2, dtype=torch.int64, device=dev)
+        theta = torch.zeros(K + 3, dtype=torch.float32, device=dev)
+        pred = torch.empty(n, K, dtype=torch.float32, device=dev)
+        legs = {
+            "accept_stats_us": lambda: sv.sv_accept_stats(acc_out, cu, attempted, accepted_at,
+                                                          totals),
+            "calibrate_update_us": lambda: sv.sv_calibrate_update(
+                theta, q_out, acc_out, cu, 1e-3, q_entropy=qh, q_max=qm),
+            "calibrate_predict_us": lambda: sv.sv_calibrate_predict(
+                theta, q_out, pred, q_entropy=qh, q_max=qm),
+        }
+        calibration = {key: graph_us(fn, args.steps) for key, fn in legs.items()}
 
     # ------------------------------------------------------------ CPU oracle leg
     traffic = measured_traffic(args.workload, args.mode)
@@ -539,6 +579,7 @@ def main():
         "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 4),
         "step_hbm_gbps": round((pass1_bytes + pass2_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
         "uniform_k": uniform_k,
+        "calibration": calibration,
         "draft_features": features,
         "full_k": full,
         "cpu_baseline": cpu,
