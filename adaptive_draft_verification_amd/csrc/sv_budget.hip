@@ -128,10 +128,19 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
             if (K != dl[q]) my_err |= SV_DEV_BAD_DRAFT_LEN;
             my_total += K;
             float s = 1.0f;
-            for (int j = 0; j < k_max; ++j) {
-                const int slot = r * k_max + j;
-                if (j < K) s = __fmul_rn(s, conf_s[r * kp + j]);
-                keys[j * n_req + r] = j < K ? survival_key(s, slot) : kNoSlot;
+            // eight positions at a time: their confidences are read before the
+            // products are chained, so the LDS reads overlap
+            for (int j0 = 0; j0 < k_max; j0 += 8) {
+                float cv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) cv[u] = j0 + u < K ? conf_s[r * kp + j0 + u] : 1.0f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = j0 + u;
+                    if (j >= k_max) break;
+                    if (j < K) s = __fmul_rn(s, cv[u]);
+                    keys[j * n_req + r] = j < K ? survival_key(s, r * k_max + j) : kNoSlot;
+                }
             }
         }
     }
