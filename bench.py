@@ -511,6 +511,18 @@ def main():
     # ----------------------------------------- stale-confidence budget leg
     # the pipeline that sizes B one step ahead: the step itself only allocates
     # the slots of a B already in device memory (here the budget selected above)
+    # the step's budget and pack call on its own, graph-replayed: its kernels'
+    # time without the staged loop's events around it
+    bs_kept = torch.empty(n, dtype=torch.int32, device=dev)
+    bs_budget = torch.empty(1, dtype=torch.int32, device=dev)
+    bs_cu = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    bs_maps = [torch.empty(cap, dtype=torch.int32, device=dev) for _ in range(3)]
+    budget_select_graph_us = graph_us(
+        lambda: sv.sv_budget_select_pack(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, last_d,
+                                         toks_d, bs_kept, bs_budget, bs_cu, *bs_maps, None, err,
+                                         ws=bws),
+        args.steps)
+
     al_kept = torch.empty(n, dtype=torch.int32, device=dev)
     budget_allocate_us = graph_us(
         lambda: sv.sv_budget_allocate(conf_d, dl_d, budget, al_kept, None, None, err, ws=bws),
@@ -569,6 +581,7 @@ def main():
                      "launch_us": round(roof_ms * 1e3, 2)},
         "budget_pack": "separate" if args.separate_pack else "fused",
         "budget_select_us": round(float(np.mean(stage_ms[:, 0])) * 1e3, 2),
+        "budget_select_graph_us": budget_select_graph_us,
         "budget_allocate_us": budget_allocate_us,
         "pack_us": round(float(np.mean(stage_ms[:, 1])) * 1e3, 2),
         "verify_pass1_us": round(pass1_ms * 1e3, 2),
