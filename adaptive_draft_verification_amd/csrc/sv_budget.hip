@@ -297,8 +297,8 @@ __device__ __forceinline__ void pack_prefetch(const PackOut& po, int n_req, int 
     }
 }
 
-// Called by every thread after write_kept (kept_s complete in LDS).  cu_s:
-// LDS, n_req + 1 entries; wave_tot: LDS, kWaves entries.
+// Called by every thread after write_kept and a barrier (kept_s complete in
+// LDS).  cu_s: LDS, n_req + 1 entries; wave_tot: LDS, kWaves entries.
 __device__ void pack_from_lds(const uint8_t* kept_s, int n_req, int k_max, const PackOut& po,
                               const PackIds& ids, int32_t* cu_s, int32_t* wave_tot) {
     const int tid = threadIdx.x;
