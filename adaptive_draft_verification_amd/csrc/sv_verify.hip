@@ -47,14 +47,16 @@ namespace {
 // the stream from ~5.8 to ~6.5 TB/s; 512-thread workgroups beat 256 and 1024;
 // with the dense order, parts of up to 131072 ids (one per row here) beat
 // 65536 (74.7 vs 76.8 us) and smaller parts lose more (3 parts 81, 4 parts
-// 88 us); an unroll of 8 loses to 4; bf16 draw super-groups of 512 ids per
+// 88 us); five loads in flight per thread beat four (73.1-73.5 against
+// 74.4-74.7 us adaptive, 147.8 against 149.9 full K) and three, six and eight;
+// draft rows with features keep four (five costs them occupancy); bf16 draw super-groups of 512 ids per
 // wave beat 1024 (28.4 vs 29.1 us: finer claims even out the waves' ends and
 // the second look is shorter), 1536 (30.4) and 2048 (35.2).
 #ifndef SV_PASS1_THREADS
 #define SV_PASS1_THREADS 512
 #endif
 #ifndef SV_PASS1_UNROLL
-#define SV_PASS1_UNROLL 4
+#define SV_PASS1_UNROLL 5
 #endif
 #ifndef SV_PASS1_NONTEMPORAL
 #define SV_PASS1_NONTEMPORAL 1
@@ -64,6 +66,7 @@ namespace {
 #endif
 constexpr int kThreads = SV_PASS1_THREADS;           // pass 1 workgroup
 constexpr int kUnroll = SV_PASS1_UNROLL;             // pass 1: 16-byte loads in flight per thread
+constexpr int kFeatUnroll = 4;  // draft rows with features: two more sums per element, fewer loads
 constexpr int kP2Threads = 1024;                     // pass 2 workgroup (stochastic)
 constexpr int kP2Waves = kP2Threads / kWave;
 constexpr int kDrawUnroll = SV_DRAW_UNROLL;          // 8-id groups per lane per super-group
@@ -285,12 +288,14 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
             a_t = (m == -kInf) ? 0.0f : m * c;
         }
     }
-    for (; i + (kUnroll - 1) * kThreads < nvec; i += kUnroll * kThreads) {
-        raw_t w[kUnroll];
+    // loads in flight per thread (the feature sums need registers of their own)
+    constexpr int U = FEAT ? kFeatUnroll : kUnroll;
+    for (; i + (U - 1) * kThreads < nvec; i += U * kThreads) {
+        raw_t w[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) w[u] = stream_load(vrow + i + u * kThreads);
+        for (int u = 0; u < U; ++u) w[u] = stream_load(vrow + i + u * kThreads);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             float x[E];
             V::unpack(w[u], x);
 #pragma unroll
