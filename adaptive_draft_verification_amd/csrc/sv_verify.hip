@@ -582,7 +582,6 @@ struct Geom {
     static constexpr int kU = DT == SV_BF16 ? kDrawUnroll : (kDrawUnroll + 1) / 2;
     static constexpr int kIds = kWave * 8 * kU;
     static constexpr int kMaxGroups = (SV_MAX_VOCAB + kIds - 1) / kIds;
-    static constexpr int kGroupsPerLane = (kMaxGroups + kWave - 1) / kWave;
     static constexpr int kIdsPerLane = kIds / kWave;  // second look: one lane's ids
 };
 constexpr int kMaxGroupsAny = Geom<SV_F32>::kMaxGroups > Geom<SV_BF16>::kMaxGroups
@@ -669,7 +668,6 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
                         bool claims_ready = false) {
     using G = Geom<DT>;
     constexpr int kGroupIds = G::kIds;
-    constexpr int kGroupsPerLane = G::kGroupsPerLane;
     constexpr int kIdsPerLane = G::kIdsPerLane;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -726,12 +724,13 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
 
     // ---- 2. walk and second look (wave 0)
     if (wave == 0) {
-        // lane l owns super-groups [l G, (l + 1) G), G = kGroupsPerLane
+        // lane l owns super-groups [l G, (l + 1) G), G = ceil(n_groups / 64):
+        // every lane a few, however long the row
+        const int gpl = (n_groups + kWave - 1) / kWave;
         float lsum = 0.0f;
         bool lpos = false;
-#pragma unroll
-        for (int i = 0; i < kGroupsPerLane; ++i) {
-            const int g = lane * kGroupsPerLane + i;
+        for (int i = 0; i < gpl; ++i) {
+            const int g = lane * gpl + i;
             if (g < n_groups) {
                 lsum += sm.gsum[g];
                 lpos |= sm.gsum[g] > 0.0f;
@@ -753,8 +752,8 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
             // lane hl's super-groups, one per lane, with a wave scan: the
             // running sum before and after each
             const float base = __shfl(incl - lsum, hl);  // exclusive prefix of lane hl
-            const int gi = hl * kGroupsPerLane + lane;
-            const float x = (lane < kGroupsPerLane && gi < n_groups) ? sm.gsum[gi] : 0.0f;
+            const int gi = hl * gpl + lane;
+            const float x = (lane < gpl && gi < n_groups) ? sm.gsum[gi] : 0.0f;
             const float xi = wave_incl_sum_dpp(x, lane);
             const float up = __shfl_up(xi, 1);  // every lane takes part in the shuffle
             const float xe = lane == 0 ? 0.0f : up;
@@ -768,7 +767,7 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
                 crossing = false;
                 hit_lane = 63 - __builtin_clzll(__ballot(posg));
             }
-            const int hit = hl * kGroupsPerLane + hit_lane;
+            const int hit = hl * gpl + hit_lane;
             const float hit_base = __shfl(before, hit_lane);
             // second look: lane l takes ids [g0 + l n, g0 + (l + 1) n), n = kIdsPerLane
             const int e0 = hit * kGroupIds + lane * kIdsPerLane;
