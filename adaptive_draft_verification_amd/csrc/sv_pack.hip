@@ -42,13 +42,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(
             }
         }
         const int cnt = r < n_req ? b + 1 : 0;
-        const int incl = wave_incl_scan<int>(cnt, lane);
+        const int incl = wave_incl_sum_dpp<int>(cnt, lane);
         __syncthreads();  // wave_tot reuse across chunks
         if (lane == kWave - 1) wave_tot[wave] = incl;
         __syncthreads();
         if (wave == 0) {
             int t = lane < kPackWaves ? wave_tot[lane] : 0;
-            t = wave_incl_scan<int>(t, lane);
+            t = wave_incl_sum_dpp<int>(t, lane);
             if (lane < kPackWaves) wave_tot[lane] = t;
         }
         __syncthreads();
