@@ -32,7 +32,8 @@
 // uniforms of the kept positions, tests u < 2^(log2 p(d) - log2 q(d)) (greedy:
 // d == argmax) and takes the first rejection with a ballot.  The token at L
 // is drawn by inverse CDF over the residual row (or the bonus row): waves
-// claim 512-id super-groups from an LDS counter and stream them (the next
+// claim super-groups (512 ids; 1024 on a bf16 bonus row) from an LDS
+// counter and stream them (the next
 // one's loads in flight while the current one is summed, no barrier in the
 // stream), each super-group's sum goes to LDS, and wave 0 walks the sums in
 // id order and reads only the crossing super-group again.
@@ -574,19 +575,22 @@ __device__ __forceinline__ void weights_from(const float* zp, const float* zq, f
     }
 }
 
-// Draw geometry: a super-group is Geom<DT>::kIds consecutive ids, one wave's
-// unit of work in the sweep (lane l takes the 8-id groups at 8 l + 512 u,
-// u < U; fp32 rows take half as many groups per lane: twice the registers).
-template <sv_dtype DT>
+// Draw geometry: a super-group is Geom<DT, RESID>::kIds consecutive ids, one
+// wave's unit of work in the sweep (lane l takes the 8-id groups at 8 l + 512 u,
+// u < U).  A residual draw reads two rows per id, a bonus draw one: bf16 bonus
+// rows take two groups per lane (the loads in flight of a residual draw's
+// one), fp32 rows one either way (twice the registers per group).
+template <sv_dtype DT, bool RESID>
 struct Geom {
-    static constexpr int kU = DT == SV_BF16 ? kDrawUnroll : (kDrawUnroll + 1) / 2;
+    static constexpr int kU = DT == SV_BF16 ? (RESID ? kDrawUnroll : 2 * kDrawUnroll)
+                                            : (kDrawUnroll + 1) / 2;
     static constexpr int kIds = kWave * 8 * kU;
     static constexpr int kMaxGroups = (SV_MAX_VOCAB + kIds - 1) / kIds;
     static constexpr int kIdsPerLane = kIds / kWave;  // second look: one lane's ids
 };
-constexpr int kMaxGroupsAny = Geom<SV_F32>::kMaxGroups > Geom<SV_BF16>::kMaxGroups
-                                  ? Geom<SV_F32>::kMaxGroups
-                                  : Geom<SV_BF16>::kMaxGroups;
+constexpr int kMaxGroupsAny = Geom<SV_F32, true>::kMaxGroups > Geom<SV_BF16, true>::kMaxGroups
+                                  ? Geom<SV_F32, true>::kMaxGroups
+                                  : Geom<SV_BF16, true>::kMaxGroups;
 
 struct DrawSmem {
     float gsum[kMaxGroupsAny];  // per super-group weight sums
@@ -614,15 +618,15 @@ struct DrawRow {
 // A super-group's raw words for one lane: U 8-id groups of each row.
 template <sv_dtype DT, bool RESID>
 struct GroupRaw {
-    Raw8<DT> p[Geom<DT>::kU], q[Geom<DT>::kU];
+    Raw8<DT> p[Geom<DT, RESID>::kU], q[Geom<DT, RESID>::kU];
 };
 
 template <sv_dtype DT, bool RESID>
 __device__ __forceinline__ void group_fetch(const DrawRow& d, int g, int lane,
                                             GroupRaw<DT, RESID>& r) {
-    const int e = g * Geom<DT>::kIds + lane * 8;
+    const int e = g * Geom<DT, RESID>::kIds + lane * 8;
 #pragma unroll
-    for (int u = 0; u < Geom<DT>::kU; ++u) {
+    for (int u = 0; u < Geom<DT, RESID>::kU; ++u) {
         r.p[u].fetch(d.prow, e + u * kWave * 8);
         if (RESID) r.q[u].fetch(d.qrow, e + u * kWave * 8);
     }
@@ -633,10 +637,10 @@ __device__ __forceinline__ void group_fetch(const DrawRow& d, int g, int lane,
 template <sv_dtype DT, bool RESID>
 __device__ __forceinline__ float group_lane_sum(const DrawRow& d, int g, int lane, bool fast,
                                                 const GroupRaw<DT, RESID>& raw) {
-    const int e = g * Geom<DT>::kIds + lane * 8;
+    const int e = g * Geom<DT, RESID>::kIds + lane * 8;
     float acc = 0.0f;
 #pragma unroll
-    for (int u = 0; u < Geom<DT>::kU; ++u) {
+    for (int u = 0; u < Geom<DT, RESID>::kU; ++u) {
         float zp[8], zq[8], w[8];
         if (fast) {
             raw.p[u].unpack(zp);
@@ -666,7 +670,7 @@ template <sv_dtype DT, bool RESID>
 __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, float ap,
                         float aq, float rq, float v, DrawSmem& sm, float* mass,
                         bool claims_ready = false) {
-    using G = Geom<DT>;
+    using G = Geom<DT, RESID>;
     constexpr int kGroupIds = G::kIds;
     constexpr int kIdsPerLane = G::kIdsPerLane;
     const int tid = threadIdx.x;
