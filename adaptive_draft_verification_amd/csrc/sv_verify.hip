@@ -1039,6 +1039,24 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
             sm.fault = fault;
             if (!GREEDY) sm.draw.next = kP2Waves;  // the draw's first claims are implicit
         }
+        // Every output the draw does not decide is written now, by the lane of
+        // its position: the accepted drafts, the -1 after L, the per-position
+        // probabilities and features, and L.  The token at L follows the draw
+        // (a fault found later overwrites all of them).
+        if (!fault) {
+            int32_t* tok_out = a.out_tokens + (int64_t)r * (k_max + 1);
+            if (j <= k_max && j != L) tok_out[j] = j < L ? d : -1;
+            if (j == 0 && k_max == kWave && L != kWave) tok_out[kWave] = -1;
+            if (j < k_max) {
+                const bool has = !GREEDY && j < b;
+                const int64_t o = (int64_t)r * k_max + j;
+                if (a.out_p) a.out_p[o] = has ? sm.tpd[j] : -1.0f;
+                if (a.out_q) a.out_q[o] = has ? sm.qpd[j] : -1.0f;
+                if (a.out_qh) a.out_qh[o] = has ? sm.qh[j] : -1.0f;
+                if (a.out_qm) a.out_qm[o] = has ? sm.qm[j] : -1.0f;
+            }
+            if (j == 0) a.out_accepted[r] = L;
+        }
     }
     __syncthreads();
     if (sm.fault) {
@@ -1078,28 +1096,8 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
         emit_fault(a, r, SV_DEV_NONFINITE);
         return;
     }
-    int32_t* tok_out = a.out_tokens + (int64_t)r * (k_max + 1);
-    for (int j = tid; j <= k_max; j += blockDim.x) {
-        int t = -1;
-        if (j < L) t = a.draft_tokens[(int64_t)r * k_max + j];
-        else if (j == L) t = token;
-        tok_out[j] = t;
-    }
-    for (int j = tid; j < k_max; j += blockDim.x) {
-        float p = -1.0f, q = -1.0f, qh = -1.0f, qm = -1.0f;
-        if (!GREEDY && j < b) {
-            p = sm.tpd[j];
-            q = sm.qpd[j];
-            qh = sm.qh[j];
-            qm = sm.qm[j];
-        }
-        if (a.out_p) a.out_p[(int64_t)r * k_max + j] = p;
-        if (a.out_q) a.out_q[(int64_t)r * k_max + j] = q;
-        if (a.out_qh) a.out_qh[(int64_t)r * k_max + j] = qh;
-        if (a.out_qm) a.out_qm[(int64_t)r * k_max + j] = qm;
-    }
     if (tid == 0) {
-        a.out_accepted[r] = L;
+        a.out_tokens[(int64_t)r * (k_max + 1) + L] = token;
         if (a.out_resid) a.out_resid[r] = (!GREEDY && L < b) ? mass : -1.0f;
     }
 }
