@@ -206,9 +206,9 @@ def cpu_baseline(args, w, tgt_full, drf_full, toks_np):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}); the verify step shards by request with no "
-              f"exchange, see the design notes.", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); the verify step would shard by request with "
+              f"no exchange.", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_calibration_mib > 0:
