@@ -210,7 +210,7 @@ __device__ __forceinline__ T waves_before(const T* tot, int wave, int lane, T* a
     const T x = lane < kWaves ? tot[lane] : T(0);
     const T incl = wave_incl_sum_dpp<T>(x, lane);
     *all = lane63(incl);
-    return __shfl(incl - x, wave);
+    return readlane_t(incl - x, wave);
 }
 
 // (score, B) pair; the better one has the larger score, then the smaller B.

@@ -25,47 +25,13 @@ __device__ __forceinline__ bool is_finite_bits(float x) {
     return (__float_as_uint(x) & 0x7fffffffu) < 0x7f800000u;
 }
 
+// Whole-wave reductions, every lane gets the result.  They go through the DPP
+// scan below (a few cycles a step) rather than LDS permutes (hundreds of
+// cycles a dependent step when the waves of a workgroup all reduce at once).
 template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ int wave_or_int(int v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o);
-    return v;
-}
-
-// Inclusive wave scan (Hillis-Steele over 64 lanes).
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        T t = __shfl_up(v, o);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
+__device__ __forceinline__ T wave_sum(T v);
+__device__ __forceinline__ float wave_max(float v);
+__device__ __forceinline__ int wave_or_int(int v);
 
 // ------------------------------------------------------------ DPP lane moves
 // Cross-lane moves through the VALU's data-parallel-primitive path (a few
@@ -99,6 +65,19 @@ __device__ __forceinline__ T lane63(T v) {
     __builtin_memcpy(w, &v, sizeof(T));
 #pragma unroll
     for (int i = 0; i < (int)(sizeof(T) / 4); ++i) w[i] = __builtin_amdgcn_readlane(w[i], 63);
+    T r;
+    __builtin_memcpy(&r, w, sizeof(T));
+    return r;
+}
+
+// Value of lane `src` (the same in every lane), in every lane.
+template <typename T>
+__device__ __forceinline__ T readlane_t(T v, int src) {
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+    const int l = __builtin_amdgcn_readfirstlane(src);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) w[i] = __builtin_amdgcn_readlane(w[i], l);
     T r;
     __builtin_memcpy(&r, w, sizeof(T));
     return r;
@@ -139,6 +118,26 @@ __device__ __forceinline__ T wave_incl_sum_dpp(T v, int lane) {
 template <typename T>
 __device__ __forceinline__ T wave_sum_dpp(T v, int lane) {
     return lane63(wave_scan_dpp(v, lane, AddOp{}));
+}
+
+struct MaxOp {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OrOp {
+    __device__ __forceinline__ int operator()(int a, int b) const { return a | b; }
+};
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+    return wave_sum_dpp(v, (int)__lane_id());
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    return lane63(wave_scan_dpp(v, (int)__lane_id(), MaxOp{}));
+}
+
+__device__ __forceinline__ int wave_or_int(int v) {
+    return lane63(wave_scan_dpp(v, (int)__lane_id(), OrOp{}));
 }
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As

@@ -159,6 +159,29 @@ __device__ __forceinline__ void merge_ase(float& a, float& s, float& e, float a2
     a = m;
 }
 
+// The merges as scan operators (earlier lane t, later lane v) for the DPP wave
+// reductions: a fixed combination order, the same in the plain and the
+// feature variants, so that (a, s) agree bit for bit between them.
+struct AS {
+    float a, s;
+};
+struct ASEM {
+    float a, s, e, mx;
+};
+struct MergeAsOp {
+    __device__ __forceinline__ AS operator()(AS t, AS v) const {
+        merge_as(v.a, v.s, t.a, t.s);
+        return v;
+    }
+};
+struct MergeAseOp {
+    __device__ __forceinline__ ASEM operator()(ASEM t, ASEM v) const {
+        merge_ase(v.a, v.s, v.e, t.a, t.s, t.e);
+        v.mx = fmaxf(v.mx, t.mx);
+        return v;
+    }
+};
+
 // Lower clamp of t in the entropy term: an id of logit -inf has weight 0 and
 // must add 0, not 0 * -inf.
 constexpr float kTFloor = -256.0f;
@@ -319,15 +342,16 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
     }
 
     float a = a_t;
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const float a2 = __shfl_xor(a, o), s2 = __shfl_xor(s, o);
-        if (FEAT) {
-            merge_ase(a, s, ef, a2, s2, __shfl_xor(ef, o));
-            mx = fmaxf(mx, __shfl_xor(mx, o));
-        } else {
-            merge_as(a, s, a2, s2);
-        }
+    if (FEAT) {
+        const ASEM w = lane63(wave_scan_dpp(ASEM{a, s, ef, mx}, lane, MergeAseOp{}));
+        a = w.a;
+        s = w.s;
+        ef = w.e;
+        mx = w.mx;
+    } else {
+        const AS w = lane63(wave_scan_dpp(AS{a, s}, lane, MergeAsOp{}));
+        a = w.a;
+        s = w.s;
     }
     if (lane == 0) {
         red[4 * wave] = a;
@@ -359,6 +383,23 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
     *out_a = A;
     *out_s = S;
 }
+
+// (max, lowest index reaching it, NaN seen) as a scan operator.
+struct ArgMax {
+    float best;
+    int idx;
+    int nan;
+};
+struct ArgMaxOp {
+    __device__ __forceinline__ ArgMax operator()(ArgMax t, ArgMax v) const {
+        v.nan |= t.nan;
+        if (t.best > v.best || (t.best == v.best && t.idx < v.idx)) {
+            v.best = t.best;
+            v.idx = t.idx;
+        }
+        return v;
+    }
+};
 
 // Greedy: (max, lowest index reaching it) and whether the row holds a NaN.
 template <sv_dtype DT, int T, int U>
@@ -422,15 +463,11 @@ __device__ void row_argmax(const char* row, int vocab, float* redf, int* redi, f
         }
     }
     int nan_i = nan ? 1 : 0;
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const float b2 = __shfl_xor(best, o);
-        const int i2 = __shfl_xor(bidx, o);
-        nan_i |= __shfl_xor(nan_i, o);
-        if (b2 > best || (b2 == best && i2 < bidx)) {
-            best = b2;
-            bidx = i2;
-        }
+    {
+        const ArgMax w = lane63(wave_scan_dpp(ArgMax{best, bidx, nan_i}, lane, ArgMaxOp{}));
+        best = w.best;
+        bidx = w.idx;
+        nan_i = w.nan;
     }
     if (lane == 0) {
         redf[wave] = best;
@@ -755,12 +792,14 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
             const int hl = crossing ? __builtin_ctzll(past) : 63 - __builtin_clzll(pos);
             // lane hl's super-groups, one per lane, with a wave scan: the
             // running sum before and after each
-            const float base = __shfl(incl - lsum, hl);  // exclusive prefix of lane hl
+            // exclusive prefix of lane hl (hl is the same in every lane)
+            const float base = readlane_t(incl - lsum, hl);
             const int gi = hl * gpl + lane;
             const float x = (lane < gpl && gi < n_groups) ? sm.gsum[gi] : 0.0f;
             const float xi = wave_incl_sum_dpp(x, lane);
-            const float up = __shfl_up(xi, 1);  // every lane takes part in the shuffle
-            const float xe = lane == 0 ? 0.0f : up;
+            // the lane below's inclusive sum (DPP wave_shr:1; lane 0 reads 0)
+            const float xe = __int_as_float(
+                __builtin_amdgcn_update_dpp(0, __float_as_int(xi), 0x138, 0xf, 0xf, false));
             const float before = base + xe;
             const bool posg = x > 0.0f;
             const uint64_t hitm = __ballot(crossing && posg && base + xi > tgt);
@@ -772,7 +811,7 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
                 hit_lane = 63 - __builtin_clzll(__ballot(posg));
             }
             const int hit = hl * gpl + hit_lane;
-            const float hit_base = __shfl(before, hit_lane);
+            const float hit_base = readlane_t(before, hit_lane);
             // second look: lane l takes ids [g0 + l n, g0 + (l + 1) n), n = kIdsPerLane
             const int e0 = hit * kGroupIds + lane * kIdsPerLane;
             float wts[kIdsPerLane];
