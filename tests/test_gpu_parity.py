@@ -467,6 +467,32 @@ def test_verify_ragged_vocab_and_strides(dtype, V, ld_pad, mode):
                    3, 11)
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_verify_random_shapes(seed):
+    """Seeded random shapes: batch, draft count, vocabulary (one super-group
+    to several row parts' worth of groups), row stride, dtype, mode,
+    temperature, Philox step and kept counts, each against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(1, 25))
+    k = int(rng.integers(0, 10))
+    V = int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(600, 20000)),
+                        int(rng.integers(20000, 70000))]))
+    ld_pad = int(rng.integers(0, 4))
+    dtype = torch.bfloat16 if seed % 2 == 0 else torch.float32
+    mode = "greedy" if seed % 5 == 0 else "stochastic"
+    tau = float(rng.choice([0.3, 0.7, 1.0, 1.8]))
+    step = int(rng.integers(0, 2 ** 40))
+    target, draft, toks, cu = synthetic(rng, n, k, V, scale=float(rng.choice([1.0, 3.0, 8.0])))
+    if dtype == torch.bfloat16:
+        target, draft = bf16_round(target), bf16_round(draft)
+    log(f"random shapes seed={seed}: n={n} k={k} V={V} ld_pad={ld_pad} {dtype} {mode} "
+        f"tau={tau} step={step}")
+    dmode = draft if mode == "stochastic" else None
+    g = gpu_verify(target, dmode, toks, cu, k, mode, tau, dtype, seed=seed, step=step,
+                   target_ld=V + ld_pad, draft_ld=V + ld_pad, features=seed % 3 == 0)
+    compare_verify(g, target, dmode, toks, cu, k, V, mode, tau, seed, step)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("mode", ["stochastic", "greedy"])
 @pytest.mark.parametrize("which", ["vocab", "drafts"])
