@@ -105,6 +105,24 @@ def test_clamp_and_survival_edge_cases():
     assert s[0, 1] == np.float32(2.0 ** -140) and s[0, 2] == np.float32(2.0 ** -141)
 
 
+
+def test_confidence_sign_is_dropped():
+    """A confidence is a probability (FOS "동작", step 1), so a survival is a
+    number in [0, 1] and carries no sign: -0, negative values and NaNs of either
+    sign clamp to +0 (bit pattern 0), and every survival is sign-free, so the
+    fp32 bit patterns of survivals order like their values."""
+    for c in (-0.0, -1e-45, -1.0, float("-nan"), float("nan")):
+        assert oracle.clamp_confidence(c).view(np.uint32) == 0, c
+    neg_nan = np.array([0xFFC00000], dtype=np.uint32).view(np.float32)[0]
+    conf = np.array([[0.5, -0.0, 0.5], [-0.0, 0.5, 0.5], [neg_nan, 1.0, 1.0]],
+                    dtype=np.float32)
+    s, _, _ = oracle.survival(conf, [3, 3, 3], 3)
+    assert not np.signbit(s).any()
+    np.testing.assert_array_equal(s.view(np.uint32),
+                                  np.array([[0x3F000000, 0, 0], [0, 0, 0], [0, 0, 0]],
+                                           dtype=np.uint32))
+    assert oracle.clamp_confidence(np.float32(2.0 ** -149)) == np.float32(2.0 ** -149)
+
 def exhaustive_best(s, lens, cost, t_base, n_bonus):
     """Best allocation over every (b_r) in prod {0..K_r}, exact rationals."""
     n = len(lens)

@@ -13,11 +13,13 @@ What fixes the answers here is not the oracle itself:
 """
 
 import json
+import math
 import os
 import sys
 
 import numpy as np
 import pytest
+import scipy.special
 from scipy import stats
 
 import oracle
@@ -346,3 +348,195 @@ def test_forced_replay_reports_overrides():
                         w.vocab, oracle.STOCHASTIC, w.tau, forced={r: forced_l})
     assert rep["accepted"][r] == forced_l
     assert len(rep["per_request"][r]["overridden"]) >= 1
+
+
+# ------------------------------------------------------------------ temperature
+#
+# The pages never mention a temperature; the verify step scales target and
+# draft logits alike, p = softmax(z / tau), q = softmax(z_draft / tau).  What
+# pins that scaling independently of the oracle's own code: two-point rows
+# whose softmax has a closed form, scipy's softmax on random rows, rows built
+# as tau * log(w) (whose law at tau is w / sum w by construction), and the
+# exact law of the emitted token at tau != 1 — which equals the target law only
+# if p and q are both taken at tau.
+
+def test_row_probs_two_point_closed_form():
+    # z = (0, ln 3): z / tau = (0, ln 3 / tau), so p = (1, 3^(1/tau)) / (1 + 3^(1/tau))
+    ln3 = math.log(3.0)
+    np.testing.assert_allclose(oracle.row_probs([0.0, ln3], 0.5), [0.1, 0.9], rtol=1e-13)
+    r3 = math.sqrt(3.0)
+    np.testing.assert_allclose(oracle.row_probs([0.0, ln3], 2.0),
+                               [1 / (1 + r3), r3 / (1 + r3)], rtol=1e-13)
+    # a masked id keeps probability 0 at any temperature
+    np.testing.assert_allclose(oracle.row_probs([0.0, -np.inf, ln3], 0.25),
+                               [1 / 82, 0.0, 81 / 82], rtol=1e-13)
+    # tau -> 0 concentrates on the argmax, large tau flattens
+    p = oracle.row_probs([0.0, 1.0, 2.0], 0.01)
+    assert p[2] == 1.0
+    assert p[1] == pytest.approx(math.exp(-100.0), rel=1e-12)
+    assert p[0] == pytest.approx(math.exp(-200.0), rel=1e-12)
+    np.testing.assert_allclose(oracle.row_probs([0.0, 1.0, 2.0], 1e6), [1 / 3] * 3, rtol=1e-5)
+
+
+@pytest.mark.parametrize("tau", [0.05, 0.3, 0.7, 1.8])
+def test_row_probs_matches_scipy_softmax(tau):
+    rng = np.random.default_rng(int(tau * 100))
+    z = rng.normal(0, 3, 5000)
+    z[rng.uniform(size=z.size) < 0.05] = -np.inf
+    want = scipy.special.softmax(z / tau)
+    np.testing.assert_allclose(oracle.row_probs(z, tau), want, rtol=1e-10, atol=1e-300)
+
+
+@pytest.mark.parametrize("tau", [0.25, 0.7, 3.0])
+def test_row_probs_of_scaled_log_weights(tau):
+    rng = np.random.default_rng(5)
+    w = rng.dirichlet(np.ones(64) * 0.5)
+    w[:5] = 0.0
+    w /= w.sum()
+    np.testing.assert_allclose(oracle.row_probs(tau * logits_of(w), tau), w, rtol=1e-9,
+                               atol=1e-300)
+
+
+V_TAU = 16
+
+
+def _tau_case(seed):
+    rng = np.random.default_rng(seed)
+    p0 = rng.dirichlet(np.ones(V_TAU) * 0.6)
+    q0 = rng.dirichlet(np.ones(V_TAU) * 0.6)
+    q0[:3] = 0.0  # the drafter never proposes ids 0..2
+    q0 /= q0.sum()
+    p0[5] = 0.0   # the target never emits id 5
+    p0 /= p0.sum()
+    return p0, q0
+
+
+def _draws_through_verify(monkeypatch, trows, drows, dtoks, b, tau):
+    """Token and accepted length of oracle.verify_request as functions of (u, v)."""
+    def run(u, v):
+        monkeypatch.setattr(overify, "uniforms", lambda seed, r, j, step: (u, v))
+        res = oracle.verify_request(0, trows, drows, dtoks, b, V_TAU, oracle.STOCHASTIC, tau,
+                                    0, 0)
+        return res["L"], res["tokens"][-1]
+    return run
+
+
+def _grid_law(token_of_v):
+    """Law over ids of a token that is a non-decreasing function of v on the 2**-24 grid."""
+    first = np.zeros(V_TAU + 1, dtype=np.int64)
+    for x in range(1, V_TAU + 1):
+        lo, hi = -1, GRID
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if token_of_v(mid / GRID) >= x:
+                hi = mid
+            else:
+                lo = mid
+        first[x] = hi
+    first[V_TAU] = GRID
+    return np.diff(first) / GRID
+
+
+def _emitted_law_at_tau(monkeypatch, p0, q0, tau):
+    """Law of the emitted token of a one-draft request whose logits are tau * log p0 and
+    tau * log q0, the draft drawn from q0, every decision taken by the oracle at tau."""
+    t0 = tau * logits_of(p0)
+    d0 = tau * logits_of(q0)
+    t1 = t0.copy()  # bonus row (its law is checked on its own below)
+    law = np.zeros(V_TAU)
+    res_law = None
+    for d in range(V_TAU):
+        if q0[d] == 0:
+            continue
+        run = _draws_through_verify(monkeypatch, [t0, t1], [d0], [d], 1, tau)
+        # acceptance share of the u grid (accepted iff L == 1; monotone in u)
+        if run(0.0, 0.5)[0] != 1:
+            a = 0.0
+        else:
+            lo, hi = 0, GRID
+            while hi - lo > 1:
+                mid = (lo + hi) // 2
+                if run(mid / GRID, 0.5)[0] == 1:
+                    lo = mid
+                else:
+                    hi = mid
+            a = hi / GRID
+        law[d] += q0[d] * a
+        if a < 1.0:
+            if res_law is None:  # the residual law does not depend on d
+                u_rej = (GRID - 1) / GRID
+                assert run(u_rej, 0.5)[0] == 0
+                res_law = _grid_law(lambda v: run(u_rej, v)[1])
+            law += q0[d] * (1.0 - a) * res_law
+    return law
+
+
+def _bonus_law_at_tau(monkeypatch, p0, tau):
+    run = _draws_through_verify(monkeypatch, [tau * logits_of(p0)], [], [], 0, tau)
+    return _grid_law(lambda v: run(0.0, v)[1])
+
+
+@pytest.mark.parametrize("tau", [0.5, 0.7, 1.8])
+def test_exact_enumeration_at_temperature(monkeypatch, tau):
+    """At tau != 1 the emitted token's law must be p = softmax(z / tau), for the
+    first position and for the bonus draw (FOS "속도, 메모리, 정확도에 주는 영향",
+    row 정확도: the output keeps the target's distribution)."""
+    p0, q0 = _tau_case(int(tau * 10))
+    np.testing.assert_allclose(_emitted_law_at_tau(monkeypatch, p0, q0, tau), p0, atol=4e-6)
+    np.testing.assert_allclose(_bonus_law_at_tau(monkeypatch, p0, tau), p0, atol=4e-6)
+
+
+@pytest.mark.parametrize("mutation", ["times_tau", "tau_ignored", "draft_at_one",
+                                      "target_at_one"])
+def test_temperature_enumeration_catches_planted_mistakes(monkeypatch, mutation):
+    """Temperature slips planted in the oracle (CPU only) must break the law at tau = 0.5."""
+    tau = 0.5
+    p0, q0 = _tau_case(3)
+    orig = overify.row_probs
+    drafts = []
+
+    def planted(z, t):
+        is_draft = any(z is dr for dr in drafts)
+        if mutation == "times_tau":
+            return orig(np.asarray(z, dtype=np.float64) * t * t, t)  # z * tau
+        if mutation == "tau_ignored":
+            return orig(z, 1.0)
+        if mutation == "draft_at_one" and is_draft:
+            return orig(z, 1.0)
+        if mutation == "target_at_one" and not is_draft:
+            return orig(z, 1.0)
+        return orig(z, t)
+
+    real_request = overify.verify_request
+
+    def spy(r, trows, drows, *args, **kw):
+        drafts[:] = list(drows)
+        return real_request(r, trows, drows, *args, **kw)
+
+    monkeypatch.setattr(overify, "row_probs", planted)
+    monkeypatch.setattr(oracle, "verify_request", spy)
+    law = _emitted_law_at_tau(monkeypatch, p0, q0, tau)
+    bonus = _bonus_law_at_tau(monkeypatch, p0, tau)
+    worst = max(np.abs(law - p0).max(), np.abs(bonus - p0).max())
+    assert worst > 1e-3, (mutation, worst)
+
+
+def test_stochastic_golden_at_temperature(monkeypatch):
+    """Hand-derived cases at tau != 1 (tests/golden/verify_stochastic_tau.json):
+    logits tau * ln(w), so the law at tau is w."""
+    g = load("verify_stochastic_tau.json")
+    for case in g["cases"]:
+        tau = case["tau"]
+        us, vs = case["u"], case["v"]
+        monkeypatch.setattr(overify, "uniforms",
+                            lambda seed, r, j, step, us=us, vs=vs: (us[j], vs[j]))
+        b = len(case["draft"])
+        V = len(case["p"][0])
+        res = oracle.verify_request(0, [tau * logits_of(p) for p in case["p"]],
+                                    [tau * logits_of(q) for q in case["q"]], case["draft"], b,
+                                    V, oracle.STOCHASTIC, tau, 0, 0)
+        assert res["tokens"] == case["tokens"], case["name"]
+        assert res["L"] == case["accepted"], case["name"]
+        np.testing.assert_allclose(res["p_d"], case["p_d"], rtol=1e-12, err_msg=case["name"])
+        np.testing.assert_allclose(res["q_d"], case["q_d"], rtol=1e-12, err_msg=case["name"])
+        assert res["residual_mass"] == pytest.approx(case["residual_mass"], abs=1e-12)
