@@ -25,6 +25,7 @@ SV_STOCHASTIC, SV_GREEDY = 0, 1
 SV_DEV_BAD_CU_ROWS, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE = 1, 2, 4
 SV_DEV_BAD_DRAFT_LEN, SV_DEV_BAD_COST, SV_DEV_BAD_KEPT = 8, 16, 32
 SV_MAX_BUDGET_SLOTS, SV_MAX_DRAFT, SV_MAX_VOCAB = 8192, 64, 1048576
+SV_MAX_VERIFY_SLOTS = 524288
 
 EXPORTED = ["sv_status_str", "sv_budget_workspace_bytes", "sv_verify_workspace_bytes",
             "sv_cost_table_prepare", "sv_budget_select", "sv_budget_allocate",

@@ -41,7 +41,9 @@ size_t sv_budget_workspace_bytes(int32_t n_req, int32_t k_max) {
 }
 
 size_t sv_verify_workspace_bytes(int32_t n_req, int32_t k_max) {
-    if (n_req < 0 || k_max < 0) return 0;
+    if (n_req < 0 || k_max < 0 || k_max > SV_MAX_DRAFT ||
+        (int64_t)n_req * (2 * k_max + 1) > SV_MAX_VERIFY_SLOTS)
+        return 0;
     return sv::verify_workspace_bytes(n_req, k_max);
 }
 
@@ -216,6 +218,7 @@ sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
     if (mode != SV_STOCHASTIC && mode != SV_GREEDY) return SV_ERR_VALUE;
     if (n_req < 0 || k_max < 0 || k_max > SV_MAX_DRAFT) return SV_ERR_SHAPE;
+    if ((int64_t)n_req * (2 * k_max + 1) > SV_MAX_VERIFY_SLOTS) return SV_ERR_SHAPE;
     if (vocab < 1 || vocab > SV_MAX_VOCAB) return SV_ERR_SHAPE;
     if (target_rows < 0 || target_ld < vocab) return SV_ERR_SHAPE;
     const bool stochastic = mode == SV_STOCHASTIC;

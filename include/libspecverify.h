@@ -65,13 +65,15 @@ typedef enum { SV_STOCHASTIC = 0, SV_GREEDY = 1 } sv_mode;
 #define SV_MAX_BUDGET_SLOTS 8192   /* n_req and n_req * k_max for sv_budget_select (LDS-resident) */
 #define SV_MAX_DRAFT        64     /* k_max for sv_verify (one wave64 ballot covers a request) and sv_budget_select */
 #define SV_MAX_VOCAB        1048576
+#define SV_MAX_VERIFY_SLOTS 524288     /* n_req * (2*k_max + 1) for sv_verify: its pass-1 grid (up to
+                                           8 parts of 512 threads per row slot) stays below 2^32 work-items */
 
 const char* sv_status_str(sv_status s);
 
 /*
- * Workspace bytes the device calls need (0 = none; pass ws = NULL then).
- * sv_verify keeps one 16-byte statistics record per candidate row part and
- * one 8-byte feature record per draft row part.
+ * Workspace bytes the device calls need (0 = none; pass ws = NULL then; also 0
+ * for shapes the call rejects).  sv_verify keeps one 16-byte statistics record
+ * per candidate row part and one 8-byte feature record per draft row part.
  */
 size_t sv_budget_workspace_bytes(int32_t n_req, int32_t k_max);
 size_t sv_verify_workspace_bytes(int32_t n_req, int32_t k_max);
@@ -316,9 +318,9 @@ sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
  * workgroups beyond the kept rows do nothing).  Pass 2: one workgroup per request (1024 threads
  * stochastic, 64 greedy) merges the parts, decides and draws.
  * Errors: SV_ERR_NULL; SV_ERR_DTYPE; SV_ERR_SHAPE if n_req < 0, k_max outside
- * [0, SV_MAX_DRAFT], vocab outside [1, SV_MAX_VOCAB], a stride below vocab or
- * target_rows < 0; SV_ERR_VALUE for an unknown mode or a bad temperature;
- * SV_ERR_WORKSPACE.
+ * [0, SV_MAX_DRAFT], n_req * (2*k_max + 1) > SV_MAX_VERIFY_SLOTS, vocab outside
+ * [1, SV_MAX_VOCAB], a stride below vocab or target_rows < 0; SV_ERR_VALUE for
+ * an unknown mode or a bad temperature; SV_ERR_WORKSPACE.
  */
 sv_status sv_verify(const void* target_logits, int64_t target_ld, int64_t target_rows,
                     const void* draft_logits, int64_t draft_ld, sv_dtype dtype, int32_t vocab,

@@ -48,6 +48,9 @@ def test_workspace_sizes():
     # 8-byte feature record per part of each of the K draft rows
     assert sv.sv_verify_workspace_bytes(256, 7) == 256 * 15 * 8 * 16 + 256 * 7 * 8 * 8
     assert sv.sv_verify_workspace_bytes(-1, 7) == 0
+    assert sv.sv_verify_workspace_bytes(1, 65) == 0
+    assert sv.sv_verify_workspace_bytes(sv.SV_MAX_VERIFY_SLOTS // 15 + 1, 7) == 0
+    assert sv.sv_verify_workspace_bytes(sv.SV_MAX_VERIFY_SLOTS // 15, 7) > 0
     # a 16-byte header, then an int32 rank and an fp32 survival per slot
     assert sv.sv_budget_workspace_bytes(256, 7) == 16 + 1792 * 8
     assert sv.sv_budget_workspace_bytes(8192, 1) == 16 + 8192 * 8
@@ -213,6 +216,14 @@ def test_verify_host_validation():
     assert verify(mode=5) == sv.SV_ERR_VALUE
     assert verify(n_req=-1) == sv.SV_ERR_SHAPE
     assert verify(k_max=65) == sv.SV_ERR_SHAPE
+    # the batch bound: n_req * (2 k_max + 1) row slots at most SV_MAX_VERIFY_SLOTS, so
+    # that the pass-1 grid (up to 8 parts of 512 threads per slot) stays below 2^32
+    # work-items; checked before the workspace, which is then sized 0
+    big = sv.SV_MAX_VERIFY_SLOTS // 15
+    assert verify(n_req=big + 1, k_max=7, ws_bytes=2**62) == sv.SV_ERR_SHAPE
+    assert verify(n_req=2**31 - 1, k_max=64, ws_bytes=2**62) == sv.SV_ERR_SHAPE
+    assert verify(n_req=big, k_max=7, ws=None) == sv.SV_ERR_WORKSPACE
+    assert sv.SV_MAX_VERIFY_SLOTS * 8 * 512 < 2**32
     assert verify(vocab=0) == sv.SV_ERR_SHAPE
     assert verify(vocab=2**20 + 1, target_ld=2**21, draft_ld=2**21) == sv.SV_ERR_SHAPE
     assert verify(target_ld=31) == sv.SV_ERR_SHAPE
@@ -280,3 +291,12 @@ def test_binding_rejects_host_tensors():
     conf = torch.zeros(2, 2)
     with pytest.raises(ValueError):
         sv.budget_select(conf, torch.zeros(2, dtype=torch.int32), torch.ones(9), 2, 2)
+
+
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    defines = dict(re.findall(r"#define\s+(SV_\w+)\s+(\d+)", text))
+    assert "SV_MAX_VERIFY_SLOTS" in defines
+    for name, value in defines.items():
+        if hasattr(sv, name):
+            assert getattr(sv, name) == int(value), name
