@@ -16,8 +16,9 @@ Comparison rules:
   the oracle is replayed with the GPU's accepted length and every overridden
   decision must lie in that band);
 * a stochastic token may differ only where the oracle's v * W lies within
-  1e-5 * W of every cumulative-sum boundary between the two ids, and the
-  GPU's id must carry positive weight;
+  the band that the probability tolerance leaves on the cumulative weights,
+  at every boundary between the two ids (``cdf_band``), and the GPU's id must
+  carry positive weight (up to that tolerance for a residual);
 * a residual whose oracle mass is below the mass floor (1e-7) is empty to
   fp32, so the zero-mass fallback (a draw from p at that row) may apply: the
   GPU's id then only has to lie in p's support;
@@ -238,20 +239,38 @@ def compare_verify(g, target, draft, draft_tokens, cu_rows, k_max, vocab, mode, 
                 assert 0 <= gt < vocab and p_l[gt] > 0, (r, gt)
                 stats["degenerate"] += 1
                 continue
-            if replayed and Lg < b and res["residual_mass"] < 1e-3:
-                stats["degenerate"] += 1  # near-empty residual after a band decision
-                continue
             full = oracle.verify_request(r, _rows_t(target, cu_rows, r, b),
                                          _rows_d(draft, r, k_max, b), draft_tokens[r], b, vocab,
                                          om, tau, seed, step, forced_l=Lg, keep_weights=True)
             w, v = full["weights"], full["v"]
-            c = np.cumsum(w)
-            t = v * c[-1]
+            assert 0 <= gt < vocab, (r, gt)
+            p_l = oracle.row_probs(target[int(cu_rows[r]) + Lg, :vocab], tau)
+            if Lg < b:  # residual max(0, p - q) of target row Lg and draft row Lg
+                q_l = oracle.row_probs(draft[r * k_max + Lg, :vocab], tau)
+                assert p_l[gt] > 0 and p_l[gt] >= q_l[gt] * (1 - 2 * P_RTOL), (r, gt)
+            else:       # bonus draw from p
+                q_l = np.zeros_like(p_l)
+                assert p_l[gt] > 0, (r, gt)
             lo, hi = min(gt, ot), max(gt, ot)
-            assert 0 <= gt < vocab and w[gt] > 0, (r, gt)
-            assert np.all(np.abs(c[lo:hi] - t) <= CDF_BAND * c[-1]), (r, gt, ot)
+            band = cdf_band(p_l, q_l, v)
+            c = np.cumsum(w)
+            assert np.all(np.abs(c[lo:hi] - v * c[-1]) <= band[lo:hi]), (r, gt, ot)
             stats["cdf_band"] += 1
     return stats
+
+
+def cdf_band(p, q, v):
+    """Per-boundary tolerance of a draw's cumulative weights, in units of p's mass.
+
+    The draw's weights are max(0, p - q) (a residual) or p (a bonus draw, q = 0).
+    With every probability allowed a relative error CDF_BAND (the tolerance of
+    p(d) and q(d)), a weight may move by CDF_BAND * (p_x + q_x), the running sum
+    C(x) by CDF_BAND * (P(x) + Q(x)) with P, Q the running sums of p and q, and
+    the target v * W by v * CDF_BAND * (P + Q over the whole row).  A boundary x
+    is ambiguous when |C(x) - v * W| is within the sum of the two.
+    """
+    P, Q = np.cumsum(p), np.cumsum(q)
+    return CDF_BAND * (P + Q + v * (P[-1] + Q[-1]))
 
 
 def _rows_t(target, cu_rows, r, b):
