@@ -138,13 +138,26 @@ struct Vec<SV_F32> {
 };
 
 
+// s * 2^d for d <= 0 without the flush of v_exp_f32 below 2^-126: the
+// fractional part through exp2 (a factor in [1, 2)), the integer part through
+// ldexp (an exact power-of-two scaling with gradual underflow).  A sum that
+// is large in its own scale keeps its share when its offset lies far below
+// the other's.  d below -300 scales any finite sum to 0.
+__device__ __forceinline__ float scale_exp2(float s, float d) {
+    const float k = floorf(fmaxf(d, -300.0f));
+    return ldexpf(s * fast_exp2(d - k), (int)k);
+}
+
 // Merge two (offset, sum) pairs: both sums re-expressed against the larger
-// offset.  The fused multiply-add is spelled out so that every caller rounds
-// alike (the compiler may otherwise fuse either product).
+// offset.  A pair without mass (s = 0: a thread or part that met no finite
+// logit, whatever offset it carries) is the identity, so it never moves the
+// offset.  A NaN sum propagates.
 __device__ __forceinline__ void merge_as(float& a, float& s, float a2, float s2) {
     const float m = fmaxf(a, a2);
-    s = fmaf(s, fast_exp2(a - m), s2 * fast_exp2(a2 - m));
-    a = m;
+    const float sm = scale_exp2(s, a - m) + scale_exp2(s2, a2 - m);
+    const bool keep = s2 == 0.0f, take = s == 0.0f;
+    s = keep ? s : (take ? s2 : sm);
+    a = keep ? a : (take ? a2 : m);
 }
 
 // Draft-row features carry e = sum_x 2^(t_x) t_x, t_x = y_x - a, next to the
@@ -153,10 +166,12 @@ __device__ __forceinline__ void merge_as(float& a, float& s, float a2, float s2)
 __device__ __forceinline__ void merge_ase(float& a, float& s, float& e, float a2, float s2,
                                           float e2) {
     const float m = fmaxf(a, a2);
-    const float f1 = fast_exp2(a - m), f2 = fast_exp2(a2 - m);
-    e = fmaf(f1, fmaf(a - m, s, e), f2 * fmaf(a2 - m, s2, e2));
-    s = fmaf(s, f1, s2 * f2);
-    a = m;
+    const float sm = scale_exp2(s, a - m) + scale_exp2(s2, a2 - m);
+    const float em = scale_exp2(fmaf(a - m, s, e), a - m) + scale_exp2(fmaf(a2 - m, s2, e2), a2 - m);
+    const bool keep = s2 == 0.0f, take = s == 0.0f;
+    s = keep ? s : (take ? s2 : sm);
+    e = keep ? e : (take ? e2 : em);
+    a = keep ? a : (take ? a2 : m);
 }
 
 // The merges as scan operators (earlier lane t, later lane v) for the DPP wave
@@ -284,6 +299,10 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
     }
     float mx = -kInf;
     float a_t = 0.0f;
+    // dflt: the thread's first element(s) held no finite logit, so its offset
+    // defaulted to 0 and its later terms below 2^-126 flushed to 0 (which
+    // matters only when the whole part lies below about 2^-86, see below)
+    bool dflt = false;
     // one element: its weight into acc, and with FEAT its entropy term and max
     auto add = [&](float x, int k) {
         const float t = fmaf(x, c, -a_t);
@@ -301,7 +320,8 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         float m = x[0];
 #pragma unroll
         for (int k = 1; k < E; ++k) m = fmaxf(m, x[k]);
-        a_t = (m == -kInf) ? 0.0f : m * c;
+        dflt = m == -kInf;
+        a_t = dflt ? 0.0f : m * c;
 #pragma unroll
         for (int k = 0; k < E; ++k) add(x[k], k);
         i += kThreads;
@@ -309,7 +329,8 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         const int e = nvec * E + tid;
         if (e < vocab) {
             const float m = V::load1(row, e);
-            a_t = (m == -kInf) ? 0.0f : m * c;
+            dflt = m == -kInf;
+            a_t = dflt ? 0.0f : m * c;
         }
     }
     // loads in flight per thread (the feature sums need registers of their own)
@@ -361,7 +382,7 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
             red[4 * wave + 3] = mx;
         }
     }
-    __syncthreads();
+    const bool any_dflt = __syncthreads_or(dflt ? 1 : 0) != 0;
     float A = red[0], S = red[1], EF = FEAT ? red[2] : 0.0f, MX = FEAT ? red[3] : -kInf;
     for (int w = 1; w < kThreads / kWave; ++w) {
         if (FEAT) {
@@ -372,13 +393,29 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         }
     }
     __syncthreads();
+    // Exact path (block-uniform): a NaN or +inf, no mass, an overflowed sum,
+    // or a thread whose offset defaulted to 0 while the part's whole mass
+    // 2^A S lies below 2^-64 (its terms below 2^-126 were flushed, and terms
+    // within 2^-40 of that mass may be among them).
     if (!(S > 0.0f) || !is_finite_bits(S) || !is_finite_bits(A) ||
-        (FEAT && !is_finite_bits(EF))) {
-        // block-uniform branch
+        (FEAT && !is_finite_bits(EF)) || (any_dflt && A + log2f(S) < -64.0f)) {
         row_stats_exact<DT, FEAT>(row, vocab, c, red, &A, &S, feat);
-    } else if (FEAT) {
-        feat->e = EF;
-        feat->mx = MX;
+    } else {
+        // A sum far from 1 (offsets well below the part's largest logit, or a
+        // defaulted offset above it) is brought to [1/2, 1) by moving the
+        // offset, so that the second pass's partial sums of 2^(y - A) cannot
+        // overflow and its terms within 2^-40 of the mass stay normal.
+        if (!(S >= 0x1p-64f && S <= 0x1p64f)) {
+            int k;
+            frexpf(S, &k);
+            if (FEAT) EF = ldexpf(fmaf(-(float)k, S, EF), -k);
+            S = ldexpf(S, -k);
+            A += (float)k;
+        }
+        if (FEAT) {
+            feat->e = EF;
+            feat->mx = MX;
+        }
     }
     *out_a = A;
     *out_s = S;
@@ -980,7 +1017,7 @@ __device__ __forceinline__ RowMerged merge_parts(const RowParts& rp, int parts, 
             if (h >= parts) break;
             if (p[h].s > 0.0f) {
                 const FeatPart f = fs.f[h];
-                e += fast_exp2(p[h].a - m.A) * fmaf(p[h].a - m.A, p[h].s, f.e);
+                e += scale_exp2(fmaf(p[h].a - m.A, p[h].s, f.e), p[h].a - m.A);
                 mx = fmaxf(mx, f.mx);
             }
         }
@@ -1333,7 +1370,7 @@ hipError_t launch_typed(const VerifyArgs& v, hipStream_t stream) {
     const int slots = GREEDY ? v.k_max + 1 : 2 * v.k_max + 1;
     if (v.stages & 1) {
         const int parts = host_row_parts(v.vocab);
-        const dim3 grid((unsigned)(v.n_req * slots * parts));
+        const dim3 grid((unsigned)((int64_t)v.n_req * slots * parts));  // < 2^23 (host-checked)
         if constexpr (GREEDY)
             hipLaunchKernelGGL((rowstats_kernel<DT, true, false>), grid, dim3(kGreedyThreads), 0, stream,
                                a, v.n_req, parts);

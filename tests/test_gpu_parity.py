@@ -645,6 +645,117 @@ def test_verify_draw_lands_on_positive_weight():
         assert (g["tokens"][rej, 0] % 2 == 0).all()
 
 
+def _far_rows(rng, n, k, V, center, spread, masked, tau):
+    """n requests at full K whose target and draft rows are center + spread * N(0, 1),
+    the first `masked` ids of every row -inf; draft ids drawn from the draft rows at tau."""
+    kept = np.full(n, k)
+    cu = np.concatenate([[0], np.cumsum(kept + 1)]).astype(np.int32)
+    target = (center + spread * rng.standard_normal((int(cu[-1]), V))).astype(np.float32)
+    target[:, :masked] = -np.inf
+    draft = np.empty((n * k, V), dtype=np.float32)
+    toks = np.empty((n, k), dtype=np.int32)
+    for r in range(n):
+        for j in range(k):
+            row = target[cu[r] + j] + (0.3 * spread * rng.standard_normal(V)).astype(np.float32)
+            draft[r * k + j] = row
+            toks[r, j] = int(np.argmax(row / tau - np.log(rng.standard_exponential(V))))
+    return target, draft, toks, cu
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("V,center,spread,masked,tau", [
+    (5000, -86.0, 1.0, 2048, 1.0),      # masked prefix, mass near 2^-124
+    (3000, -88.0, 1.0, 0, 1.0),         # short row: threads without ids
+    (1003, -88.0, 1.0, 0, 1.0),
+    (4095, -86.0, 1.0, 0, 1.0),
+    (5000, -4.3, 0.05, 2048, 0.05),     # the same scale reached through a low temperature
+    (129280, -86.0, 1.0, 4096, 1.0),    # every thread's first chunk masked
+    (200003, -87.0, 1.0, 3000, 1.0),    # two row parts
+])
+def test_verify_far_negative_logits(dtype, V, center, spread, masked, tau):
+    """Rows whose whole mass lies near the bottom of fp32's normal range, with and
+    without a masked prefix: threads that meet no finite logit first, or no id at
+    all, must not move the row's offset, and terms that a defaulted offset would
+    flush must be recovered (the exact path)."""
+    rng = np.random.default_rng(V + masked)
+    n, k = 4, 3
+    target, draft, toks, cu = _far_rows(rng, n, k, V, center, spread, masked, tau)
+    if dtype == torch.bfloat16:
+        target, draft = bf16_round(target), bf16_round(draft)
+    log(f"far-negative V={V} center={center} masked={masked} tau={tau} {dtype}")
+    for features in (False, True):
+        g = gpu_verify(target, draft, toks, cu, k, "stochastic", tau, dtype, seed=4,
+                       features=features)
+        compare_verify(g, target, draft, toks, cu, k, V, "stochastic", tau, 4)
+        assert int(g["dev_error"][0]) == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_verify_finite_mask_far_below_the_row(dtype):
+    """Ids masked with a finite logit (-88) in every first chunk of half the
+    threads, whose later ids sit 9 below the rest: their sums are large in their
+    own scale and their offsets lie more than 126 (log2 units) below the row's,
+    so a rescale that flushed below 2^-126 would drop ~1e-4 of the mass."""
+    E = 8 if dtype == torch.bfloat16 else 4
+    rng = np.random.default_rng(61)
+    n, k, V = 3, 2, 6144
+    ids = np.arange(V)
+    base = np.where(((ids // E) % 512) < 256, -9.0, 0.0)
+    kept = np.full(n, k)
+    cu = np.concatenate([[0], np.cumsum(kept + 1)]).astype(np.int32)
+    target = (base + 0.1 * rng.standard_normal((int(cu[-1]), V))).astype(np.float32)
+    target[:, : 256 * E] = -88.0
+    draft = (target[np.repeat(np.arange(n) * (k + 1), k) + np.tile(np.arange(k), n)]
+             + 0.05 * rng.standard_normal((n * k, V))).astype(np.float32)
+    draft[:, : 256 * E] = -88.0
+    toks = rng.integers(256 * E, V, (n, k)).astype(np.int32)
+    if dtype == torch.bfloat16:
+        target, draft = bf16_round(target), bf16_round(draft)
+    for features in (False, True):
+        g = gpu_verify(target, draft, toks, cu, k, "stochastic", 1.0, dtype, seed=6,
+                       features=features)
+        compare_verify(g, target, draft, toks, cu, k, V, "stochastic", 1.0, 6)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_verify_zero_draft_probability(dtype):
+    """q(d) = 0 (a -inf draft logit at the draft id): accepted whenever p(d) > 0,
+    rejected when p(d) = 0 too (then the residual is drawn), whatever u.  Ids in
+    the first and the second row part and in the ragged tail (V = 200003: two
+    parts, V not a multiple of 8)."""
+    rng = np.random.default_rng(67)
+    n, k, V = 6, 3, 200003
+    target, draft, toks, cu = synthetic(rng, n, k, V, np.full(n, k))
+    tail, second, first = V - 1, 150001, 7
+
+    def q_zero(r, j, d, p_zero=False):
+        toks[r, j] = d
+        draft[r * k + j, d] = -np.inf
+        if p_zero:
+            target[cu[r] + j, d] = -np.inf
+
+    q_zero(0, 0, second)                 # accept at 0
+    q_zero(1, 0, first)
+    q_zero(1, 1, tail)                   # accept at 0 and 1
+    q_zero(2, 0, second, p_zero=True)    # reject at 0
+    q_zero(3, 0, tail)
+    q_zero(3, 1, first)
+    q_zero(3, 2, tail - 1, p_zero=True)  # accept 0, 1; reject at 2
+    q_zero(4, 0, first, p_zero=True)     # reject at 0
+    if dtype == torch.bfloat16:
+        target, draft = bf16_round(target), bf16_round(draft)
+    for seed in range(3):
+        g = gpu_verify(target, draft, toks, cu, k, "stochastic", 0.9, dtype, seed=seed,
+                       features=True)
+        compare_verify(g, target, draft, toks, cu, k, V, "stochastic", 0.9, seed)
+        acc = g["accepted"]
+        assert acc[0] >= 1 and acc[1] >= 2 and acc[2] == 0 and acc[3] == 2 and acc[4] == 0
+        assert g["q_draft"][0, 0] == 0 and g["p_draft"][0, 0] > 0
+        assert g["q_draft"][2, 0] == 0 and g["p_draft"][2, 0] == 0
+        assert g["tokens"][2, 0] != second and g["tokens"][4, 0] != first
+        assert g["tokens"][3, 2] != tail - 1
+
+
 def test_verify_is_deterministic_and_stream_safe():
     rng = np.random.default_rng(37)
     n, k, V = 32, 7, 50000
