@@ -19,20 +19,22 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
-SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_VALUE, SV_ERR_WORKSPACE, SV_ERR_LAUNCH = range(7)
+SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_VALUE, SV_ERR_WORKSPACE, SV_ERR_LAUNCH, \
+    SV_ERR_CAPACITY = range(8)
 SV_F32, SV_BF16 = 0, 1
 SV_STOCHASTIC, SV_GREEDY = 0, 1
 SV_DEV_BAD_CU_ROWS, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE = 1, 2, 4
 SV_DEV_BAD_DRAFT_LEN, SV_DEV_BAD_COST, SV_DEV_BAD_KEPT = 8, 16, 32
 SV_MAX_BUDGET_SLOTS, SV_MAX_DRAFT, SV_MAX_VOCAB = 8192, 64, 1048576
 SV_MAX_VERIFY_SLOTS = 524288
+SV_NOALLOC_WS_BYTES = 8388608
 
 EXPORTED = ["sv_status_str", "sv_budget_workspace_bytes", "sv_verify_workspace_bytes",
             "sv_cost_table_prepare", "sv_budget_select", "sv_budget_allocate",
             "sv_budget_select_pack", "sv_budget_allocate_pack",
             "sv_uniform_k_select", "sv_pack_varlen",
             "sv_verify",
-            "sv_verify_stages", "sv_accept_stats", "sv_calibrate_update", "sv_calibrate_predict",
+            "sv_verify_stages", "sv_verify_noalloc", "sv_accept_stats", "sv_calibrate_update", "sv_calibrate_predict",
             "sv_philox_uniforms"]
 
 
@@ -71,6 +73,9 @@ def _load():
         "sv_verify_stages": (ctypes.c_int, [vp, i64, i64, vp, i64, ctypes.c_int, i32, vp, vp, i32,
                                             i32, ctypes.c_int, f32, u64, u64, vp, vp, vp, vp, vp,
                                             vp, vp, vp, vp, sz, i32, vp]),
+        "sv_verify_noalloc": (ctypes.c_int, [vp, i64, i64, vp, i64, ctypes.c_int, i32, vp, vp,
+                                             i32, i32, ctypes.c_int, f32, u64, u64, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, vp]),
         "sv_accept_stats": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp, vp]),
         "sv_calibrate_update": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp]),
         "sv_calibrate_predict": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, vp, vp]),
@@ -325,7 +330,7 @@ def _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, 
             _ptr(draft_tokens), _ptr(cu_rows), n, k_max, int(mode), float(temperature),
             int(seed), int(step), _ptr(out_tokens), _ptr(out_accepted), _ptr(out_p_draft),
             _ptr(out_q_draft), _ptr(out_residual_mass), _ptr(out_q_entropy), _ptr(out_q_max),
-            _ptr(dev_error), _ptr(ws), ws.numel()]
+            _ptr(dev_error), _ptr(ws), 0 if ws is None else ws.numel()]
 
 
 def sv_verify(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step, out_tokens,
@@ -350,6 +355,19 @@ def sv_verify_stages(target, draft, draft_tokens, cu_rows, mode, temperature, se
                         out_tokens, out_accepted, ws, out_p_draft, out_q_draft,
                         out_residual_mass, dev_error, vocab, out_q_entropy, out_q_max)
     _check(_lib.sv_verify_stages(*args, int(stages), _stream(stream)), "sv_verify_stages")
+
+
+def sv_verify_noalloc(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
+                      out_tokens, out_accepted, out_p_draft=None, out_q_draft=None,
+                      out_residual_mass=None, dev_error=None, vocab=None, stream=None,
+                      out_q_entropy=None, out_q_max=None):
+    """sv_verify without a workspace argument: the library's static per-GPU array
+    serves as the workspace (the call allocates nothing; overlapping calls on one
+    GPU race on it)."""
+    args = _verify_args(target, draft, draft_tokens, cu_rows, mode, temperature, seed, step,
+                        out_tokens, out_accepted, None, out_p_draft, out_q_draft,
+                        out_residual_mass, dev_error, vocab, out_q_entropy, out_q_max)
+    _check(_lib.sv_verify_noalloc(*args[:-2], _stream(stream)), "sv_verify_noalloc")
 
 
 def sv_accept_stats(accepted, cu_rows, attempted, accepted_at, totals, stream=None):

@@ -23,7 +23,8 @@ LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["sv_api.cpp", "sv_budget.hip", "sv_pack.hip", "sv_verify.hip", "sv_calibrate.hip"]
+SOURCES = ["sv_api.cpp", "sv_budget.hip", "sv_pack.hip", "sv_verify.hip", "sv_calibrate.hip",
+           "sv_noalloc.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere (hipcc emits them from
 # plain float code otherwise); the host pass warns that it does not know the

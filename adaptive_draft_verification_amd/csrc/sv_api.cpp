@@ -18,6 +18,34 @@ sv_status launched(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_LAUNC
 
 }  // namespace
 
+namespace sv {
+
+sv_status check_verify(const VerifyArgs& v) {
+    if (v.dtype != SV_F32 && v.dtype != SV_BF16) return SV_ERR_DTYPE;
+    if (v.mode != SV_STOCHASTIC && v.mode != SV_GREEDY) return SV_ERR_VALUE;
+    if (v.n_req < 0 || v.k_max < 0 || v.k_max > SV_MAX_DRAFT) return SV_ERR_SHAPE;
+    if ((int64_t)v.n_req * (2 * v.k_max + 1) > SV_MAX_VERIFY_SLOTS) return SV_ERR_SHAPE;
+    if (v.vocab < 1 || v.vocab > SV_MAX_VOCAB) return SV_ERR_SHAPE;
+    if (v.target_rows < 0 || v.target_ld < v.vocab) return SV_ERR_SHAPE;
+    const bool stochastic = v.mode == SV_STOCHASTIC;
+    if (stochastic && v.draft_ld < v.vocab) return SV_ERR_SHAPE;
+    if (stochastic && (!std::isfinite(v.temperature) || !(v.temperature > 0.0f)))
+        return SV_ERR_VALUE;
+    if (v.n_req == 0) return SV_OK;
+    if (v.target == nullptr || v.cu_rows == nullptr || v.out_tokens == nullptr ||
+        v.out_accepted == nullptr)
+        return SV_ERR_NULL;
+    if (v.k_max > 0 && v.draft_tokens == nullptr) return SV_ERR_NULL;
+    if (stochastic && v.k_max > 0 && v.draft == nullptr) return SV_ERR_NULL;
+    // the largest element offset a kernel may form must fit int64
+    if ((double)v.target_rows * (double)v.target_ld > 9.0e18) return SV_ERR_SHAPE;
+    // log2(e) / T must be a finite fp32
+    if (stochastic && (1.4426950408889634 / (double)v.temperature) > 3.0e38) return SV_ERR_VALUE;
+    return SV_OK;
+}
+
+}  // namespace sv
+
 extern "C" {
 
 const char* sv_status_str(sv_status s) {
@@ -29,6 +57,7 @@ const char* sv_status_str(sv_status s) {
         case SV_ERR_VALUE: return "a scalar argument is out of range";
         case SV_ERR_WORKSPACE: return "workspace missing or too small";
         case SV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+        case SV_ERR_CAPACITY: return "the batch needs more than the static workspace holds";
     }
     return "unknown status";
 }
@@ -215,31 +244,16 @@ sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t
                            int32_t* dev_error, void* ws, size_t ws_bytes, int32_t stages,
                            void* stream) {
     if (stages < 1 || stages > 3) return SV_ERR_VALUE;
-    if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_DTYPE;
-    if (mode != SV_STOCHASTIC && mode != SV_GREEDY) return SV_ERR_VALUE;
-    if (n_req < 0 || k_max < 0 || k_max > SV_MAX_DRAFT) return SV_ERR_SHAPE;
-    if ((int64_t)n_req * (2 * k_max + 1) > SV_MAX_VERIFY_SLOTS) return SV_ERR_SHAPE;
-    if (vocab < 1 || vocab > SV_MAX_VOCAB) return SV_ERR_SHAPE;
-    if (target_rows < 0 || target_ld < vocab) return SV_ERR_SHAPE;
-    const bool stochastic = mode == SV_STOCHASTIC;
-    if (stochastic && draft_ld < vocab) return SV_ERR_SHAPE;
-    if (stochastic && (!std::isfinite(temperature) || !(temperature > 0.0f))) return SV_ERR_VALUE;
-    if (n_req == 0) return SV_OK;
-    if (target_logits == nullptr || cu_rows == nullptr || out_tokens == nullptr ||
-        out_accepted == nullptr)
-        return SV_ERR_NULL;
-    if (k_max > 0 && draft_tokens == nullptr) return SV_ERR_NULL;
-    if (stochastic && k_max > 0 && draft_logits == nullptr) return SV_ERR_NULL;
-    // the largest element offset a kernel may form must fit int64
-    if ((double)target_rows * (double)target_ld > 9.0e18) return SV_ERR_SHAPE;
+    const sv::VerifyArgs a{target_logits, target_ld,    target_rows,  draft_logits, draft_ld,
+                           dtype,         vocab,        draft_tokens, cu_rows,      n_req,
+                           k_max,         mode,         temperature,  seed,         step,
+                           out_tokens,    out_accepted, out_p_draft,  out_q_draft,
+                           out_residual_mass, out_q_entropy, out_q_max, dev_error,  ws,
+                           stages};
+    const sv_status st = sv::check_verify(a);
+    if (st != SV_OK || n_req == 0) return st;
     const size_t need = sv::verify_workspace_bytes(n_req, k_max);
     if (ws == nullptr || ws_bytes < need) return SV_ERR_WORKSPACE;
-    if (stochastic && (1.4426950408889634 / (double)temperature) > 3.0e38) return SV_ERR_VALUE;
-    sv::VerifyArgs a{target_logits, target_ld,    target_rows,  draft_logits, draft_ld,
-                     dtype,         vocab,        draft_tokens, cu_rows,      n_req,
-                     k_max,         mode,         temperature,  seed,         step,
-                     out_tokens,    out_accepted, out_p_draft,  out_q_draft,  out_residual_mass,
-                     out_q_entropy, out_q_max,    dev_error,    ws,           stages};
     return launched(sv::launch_verify(a, as_stream(stream)));
 }
 

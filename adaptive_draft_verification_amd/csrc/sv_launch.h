@@ -70,6 +70,9 @@ struct VerifyArgs {
 
 size_t verify_workspace_bytes(int n_req, int k_max);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+// sv_verify's host checks of everything but the workspace (sv_api.cpp): SV_OK means
+// a launch may follow (nothing to launch when n_req = 0).
+sv_status check_verify(const VerifyArgs& a);
 
 hipError_t launch_accept_stats(const int32_t* accepted, const int32_t* cu_rows, int n_req,
                                int k_max, uint64_t* attempted, uint64_t* accepted_at,

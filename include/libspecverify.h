@@ -47,7 +47,8 @@ typedef enum {
     SV_ERR_DTYPE = 3,     /* unknown sv_dtype                                  */
     SV_ERR_VALUE = 4,     /* a scalar is out of range (temperature, mode, ...) */
     SV_ERR_WORKSPACE = 5, /* workspace missing or smaller than required        */
-    SV_ERR_LAUNCH = 6     /* the HIP runtime refused a kernel launch           */
+    SV_ERR_LAUNCH = 6,    /* the HIP runtime refused a kernel launch           */
+    SV_ERR_CAPACITY = 7   /* the batch needs more than a static workspace holds */
 } sv_status;
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -65,6 +66,7 @@ typedef enum { SV_STOCHASTIC = 0, SV_GREEDY = 1 } sv_mode;
 #define SV_MAX_BUDGET_SLOTS 8192   /* n_req and n_req * k_max for sv_budget_select (LDS-resident) */
 #define SV_MAX_DRAFT        64     /* k_max for sv_verify (one wave64 ballot covers a request) and sv_budget_select */
 #define SV_MAX_VOCAB        1048576
+#define SV_NOALLOC_WS_BYTES 8388608   /* sv_verify_noalloc's static workspace per GPU (8 MiB) */
 #define SV_MAX_VERIFY_SLOTS 524288     /* n_req * (2*k_max + 1) for sv_verify: its pass-1 grid (up to
                                            8 parts of 512 threads per row slot) stays below 2^32 work-items */
 
@@ -350,6 +352,38 @@ sv_status sv_verify_stages(const void* target_logits, int64_t target_ld, int64_t
                            float* out_residual_mass, float* out_q_entropy, float* out_q_max,
                            int32_t* dev_error, void* ws, size_t ws_bytes, int32_t stages,
                            void* stream);
+
+/*
+ * sv_verify_noalloc — sv_verify for callers that cannot allocate device
+ * memory: work recorded under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc.  Same arguments, checks, kernels and results as
+ * sv_verify, without ws and ws_bytes: the per-part statistics pass 1 hands to
+ * pass 2 live in a static device array of SV_NOALLOC_WS_BYTES bytes, one copy
+ * per GPU, held from the library's load until the process ends (its address
+ * is looked up once per GPU, on the first call there).  The call allocates
+ * and frees nothing.
+ * Limit: sv_verify_workspace_bytes(n_req, k_max) <= SV_NOALLOC_WS_BYTES, i.e.
+ * n_req * ((2*k_max + 1) * 128 + k_max * 64) bytes (256 requests x 7 drafts:
+ * 606,208 bytes; at most 3542 requests at k_max = 7); larger batches return
+ * SV_ERR_CAPACITY before anything is launched.
+ * Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ * last call's contents (nothing in it needs clearing: every record pass 2
+ * reads is written by pass 1 of the same call).  Calls that overlap in time
+ * on one GPU (two streams, or two host threads) race on the array and must
+ * be serialised by the caller.  `stream` selects the GPU (NULL: the current
+ * device's null stream).
+ * Errors: those of sv_verify except SV_ERR_WORKSPACE; SV_ERR_CAPACITY as
+ * above; SV_ERR_LAUNCH if the runtime cannot name the stream's device or the
+ * array's address, or refuses a launch.
+ */
+sv_status sv_verify_noalloc(const void* target_logits, int64_t target_ld, int64_t target_rows,
+                            const void* draft_logits, int64_t draft_ld, sv_dtype dtype,
+                            int32_t vocab, const int32_t* draft_tokens, const int32_t* cu_rows,
+                            int32_t n_req, int32_t k_max, sv_mode mode, float temperature,
+                            uint64_t seed, uint64_t step, int32_t* out_tokens,
+                            int32_t* out_accepted, float* out_p_draft, float* out_q_draft,
+                            float* out_residual_mass, float* out_q_entropy, float* out_q_max,
+                            int32_t* dev_error, void* stream);
 
 /*
  * Acceptance statistics and online calibration of the per-position

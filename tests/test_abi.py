@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert sv.sv_status_str(s)
     assert sv.sv_status_str(99) == "unknown status"
 
@@ -300,3 +300,25 @@ def test_binding_constants_match_the_header():
     for name, value in defines.items():
         if hasattr(sv, name):
             assert getattr(sv, name) == int(value), name
+
+
+def test_verify_noalloc_host_validation():
+    """sv_verify_noalloc's checks run before any HIP call: sv_verify's own, then the
+    static workspace's capacity."""
+    def call(**kw):
+        args = dict(target=FAKE, target_ld=32, target_rows=16, draft=FAKE, draft_ld=32,
+                    dtype=sv.SV_F32, vocab=32, draft_tokens=FAKE, cu_rows=FAKE, n_req=4,
+                    k_max=3, mode=sv.SV_STOCHASTIC, temperature=1.0, seed=0, step=0,
+                    out_tokens=FAKE, out_accepted=FAKE, out_p=None, out_q=None, out_resid=None,
+                    out_qh=None, out_qm=None, dev_error=None, stream=None)
+        args.update(kw)
+        return sv._lib.sv_verify_noalloc(*args.values())
+    per_req = (2 * 7 + 1) * 128 + 7 * 64
+    over = sv.SV_NOALLOC_WS_BYTES // per_req + 1
+    assert call(n_req=over, k_max=7) == sv.SV_ERR_CAPACITY
+    assert call(n_req=over - 1, k_max=7, target=None) == sv.SV_ERR_NULL  # fits: other checks
+    assert call(dtype=9) == sv.SV_ERR_DTYPE
+    assert call(k_max=65) == sv.SV_ERR_SHAPE
+    assert call(temperature=0.0) == sv.SV_ERR_VALUE
+    assert call(n_req=0, target=None) == sv.SV_OK
+    assert sv.sv_status_str(sv.SV_ERR_CAPACITY)
