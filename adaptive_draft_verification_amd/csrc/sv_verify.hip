@@ -138,26 +138,28 @@ struct Vec<SV_F32> {
 };
 
 
-// s * 2^d for d <= 0 without the flush of v_exp_f32 below 2^-126: the
-// fractional part through exp2 (a factor in [1, 2)), the integer part through
-// ldexp (an exact power-of-two scaling with gradual underflow).  A sum that
-// is large in its own scale keeps its share when its offset lies far below
-// the other's.  d below -300 scales any finite sum to 0.
+// s * 2^d for d <= 0: 2^(d/2) squared, so that v_exp_f32's flush below 2^-126
+// bites only for d < -252 (a sum below 2^128 then adds less than 2^-124, far
+// below any sum that holds a term near 1).  A sum that is large in its own
+// scale keeps its share when its offset lies far below the other's.
 __device__ __forceinline__ float scale_exp2(float s, float d) {
-    const float k = floorf(fmaxf(d, -300.0f));
-    return ldexpf(s * fast_exp2(d - k), (int)k);
+    const float f = fast_exp2(0.5f * d);
+    return (s * f) * f;
 }
 
+// Offset of a pair without mass (a thread that met no finite logit): far
+// below any real offset, so that merging it scales its zero sum by 0 and
+// leaves the other pair as it was; two such pairs merge to one.
+constexpr float kNoMass = -1.0e30f;
+
 // Merge two (offset, sum) pairs: both sums re-expressed against the larger
-// offset.  A pair without mass (s = 0: a thread or part that met no finite
-// logit, whatever offset it carries) is the identity, so it never moves the
-// offset.  A NaN sum propagates.
+// offset (scale_exp2 spelled out with an explicit fused multiply-add, so that
+// every caller rounds alike).  A NaN sum propagates.
 __device__ __forceinline__ void merge_as(float& a, float& s, float a2, float s2) {
     const float m = fmaxf(a, a2);
-    const float sm = scale_exp2(s, a - m) + scale_exp2(s2, a2 - m);
-    const bool keep = s2 == 0.0f, take = s == 0.0f;
-    s = keep ? s : (take ? s2 : sm);
-    a = keep ? a : (take ? a2 : m);
+    const float f1 = fast_exp2(0.5f * (a - m)), f2 = fast_exp2(0.5f * (a2 - m));
+    s = fmaf(s * f1, f1, (s2 * f2) * f2);
+    a = m;
 }
 
 // Draft-row features carry e = sum_x 2^(t_x) t_x, t_x = y_x - a, next to the
@@ -166,12 +168,10 @@ __device__ __forceinline__ void merge_as(float& a, float& s, float a2, float s2)
 __device__ __forceinline__ void merge_ase(float& a, float& s, float& e, float a2, float s2,
                                           float e2) {
     const float m = fmaxf(a, a2);
-    const float sm = scale_exp2(s, a - m) + scale_exp2(s2, a2 - m);
-    const float em = scale_exp2(fmaf(a - m, s, e), a - m) + scale_exp2(fmaf(a2 - m, s2, e2), a2 - m);
-    const bool keep = s2 == 0.0f, take = s == 0.0f;
-    s = keep ? s : (take ? s2 : sm);
-    e = keep ? e : (take ? e2 : em);
-    a = keep ? a : (take ? a2 : m);
+    const float f1 = fast_exp2(0.5f * (a - m)), f2 = fast_exp2(0.5f * (a2 - m));
+    e = fmaf(fmaf(a - m, s, e) * f1, f1, (fmaf(a2 - m, s2, e2) * f2) * f2);
+    s = fmaf(s * f1, f1, (s2 * f2) * f2);
+    a = m;
 }
 
 // The merges as scan operators (earlier lane t, later lane v) for the DPP wave
@@ -281,7 +281,8 @@ __device__ void row_stats_exact(const char* row, int vocab, float c, float* red,
 // as without it.
 template <sv_dtype DT, bool FEAT = false>
 __device__ void row_stats_stochastic(const char* row, int vocab, float c, float* red,
-                                     float* out_a, float* out_s, FeatAcc* feat = nullptr) {
+                                     int* redflag, float* out_a, float* out_s,
+                                     FeatAcc* feat = nullptr) {
     using V = Vec<DT>;
     using raw_t = typename V::raw_t;
     constexpr int E = V::kElems;
@@ -362,7 +363,8 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         if (FEAT) ef += eacc[k];
     }
 
-    float a = a_t;
+    // a thread that met no finite logit (s = 0) must not move the offset
+    float a = s == 0.0f ? kNoMass : a_t;
     if (FEAT) {
         const ASEM w = lane63(wave_scan_dpp(ASEM{a, s, ef, mx}, lane, MergeAseOp{}));
         a = w.a;
@@ -374,6 +376,7 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         a = w.a;
         s = w.s;
     }
+    const bool wave_dflt = __ballot(dflt) != 0;
     if (lane == 0) {
         red[4 * wave] = a;
         red[4 * wave + 1] = s;
@@ -381,10 +384,13 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
             red[4 * wave + 2] = ef;
             red[4 * wave + 3] = mx;
         }
+        redflag[wave] = wave_dflt;
     }
-    const bool any_dflt = __syncthreads_or(dflt ? 1 : 0) != 0;
+    __syncthreads();
     float A = red[0], S = red[1], EF = FEAT ? red[2] : 0.0f, MX = FEAT ? red[3] : -kInf;
+    bool any_dflt = redflag[0] != 0;
     for (int w = 1; w < kThreads / kWave; ++w) {
+        any_dflt |= redflag[w] != 0;
         if (FEAT) {
             merge_ase(A, S, EF, red[4 * w], red[4 * w + 1], red[4 * w + 2]);
             MX = fmaxf(MX, red[4 * w + 3]);
@@ -1319,9 +1325,9 @@ __global__ __launch_bounds__(pass1_threads<GREEDY>()) void rowstats_kernel(Args 
     float A, S;
     FeatAcc fa;
     if (FEAT && is_draft)
-        row_stats_stochastic<DT, true>(prow, p1 - p0, a.c, redf, &A, &S, &fa);
+        row_stats_stochastic<DT, true>(prow, p1 - p0, a.c, redf, redi, &A, &S, &fa);
     else
-        row_stats_stochastic<DT>(prow, p1 - p0, a.c, redf, &A, &S);
+        row_stats_stochastic<DT>(prow, p1 - p0, a.c, redf, redi, &A, &S);
     if (FEAT && is_draft && threadIdx.x == 0) {
         FeatPart f;
         f.e = fa.e;
