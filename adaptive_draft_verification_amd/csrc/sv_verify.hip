@@ -8,7 +8,7 @@
 // from the normalised residual max(0, p - q)), and section "평균 수락 길이"
 // (the bonus token).
 //
-// Pass 1, one workgroup (512 threads; greedy 256) per row part: target rows
+// Pass 1, one 512-thread workgroup per row part: target rows
 // 0..b and (stochastic) draft rows 0..b-1 of each request.  The grid is the
 // host-known capacity.  With well-formed offsets workgroup u takes the u-th
 // existing row part (target rows in packed order, then draft rows), so the
@@ -72,10 +72,19 @@ constexpr int kP2Threads = 1024;                     // pass 2 workgroup (stocha
 constexpr int kP2Waves = kP2Threads / kWave;
 constexpr int kDrawUnroll = SV_DRAW_UNROLL;          // 8-id groups per lane per super-group
 // Greedy pass 1 (target rows only, a max per element instead of an exp):
-// 256-thread workgroups with six 16-byte loads in flight per thread beat the
-// stochastic shape (45.6 against 47.2 us adaptive, 84.8 against 85.8 full K).
-constexpr int kGreedyThreads = 256;
-constexpr int kGreedyUnroll = 6;
+// 512-thread workgroups with six 16-byte loads in flight per thread (full K,
+// 2048 rows of 129280 bf16: 80.5 us against 83.0 with 256 threads and 85 with
+// 1024; the adaptive batch 43.0 against 43.2); half-row parts, eight loads in
+// flight and a scheduling barrier after the loads all lost.
+#ifndef SV_GREEDY_THREADS
+#define SV_GREEDY_THREADS 512
+#endif
+#ifndef SV_GREEDY_UNROLL
+#define SV_GREEDY_UNROLL 6
+#endif
+
+constexpr int kGreedyThreads = SV_GREEDY_THREADS;
+constexpr int kGreedyUnroll = SV_GREEDY_UNROLL;
 template <bool GREEDY>
 constexpr int pass1_threads() { return GREEDY ? kGreedyThreads : kThreads; }
 
@@ -564,12 +573,12 @@ constexpr int kMaxParts = 8;
 #ifndef SV_PART_IDS
 #define SV_PART_IDS 131072
 #endif
+#ifndef SV_GREEDY_PART_IDS
+#define SV_GREEDY_PART_IDS SV_PART_IDS
+#endif
 constexpr int kPartIds = SV_PART_IDS;  // parts of about this many ids
+constexpr int kGreedyPartIds = SV_GREEDY_PART_IDS;
 
-__device__ __forceinline__ int row_parts(int vocab) {
-    const int h = (vocab + kPartIds - 1) / kPartIds;
-    return h < 1 ? 1 : (h > kMaxParts ? kMaxParts : h);
-}
 __device__ __forceinline__ int part_len(int vocab, int parts) {
     return ((vocab + parts - 1) / parts + 7) & ~7;
 }
@@ -584,6 +593,7 @@ struct Args {
     const int32_t* draft_tokens;
     const int32_t* cu_rows;
     int k_max;
+    int parts;  // row parts (pass-1 workgroups per row)
     float c;  // log2(e) / T
     uint64_t seed;
     uint64_t step;
@@ -1049,7 +1059,7 @@ template <sv_dtype DT, bool GREEDY>
 __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
     const int tid = threadIdx.x;
     const int k_max = a.k_max;
-    const int parts = row_parts(a.vocab), plen = part_len(a.vocab, parts);
+    const int parts = a.parts, plen = part_len(a.vocab, parts);
     const PartStat* st = a.stats + (int64_t)r * (2 * k_max + 1) * kMaxParts;
     if (tid < kWave) {
         // lane j: position j (target row j and draft row j); lane b also
@@ -1356,8 +1366,9 @@ size_t stats_bytes(int n_req, int k_max) {
     return (size_t)n_req * (size_t)(2 * k_max + 1) * kMaxParts * sizeof(PartStat);
 }
 
-int host_row_parts(int vocab) {
-    const int h = (vocab + kPartIds - 1) / kPartIds;
+int host_row_parts(int vocab, bool greedy) {
+    const int ids = greedy ? kGreedyPartIds : kPartIds;
+    const int h = (vocab + ids - 1) / ids;
     return h < 1 ? 1 : (h > kMaxParts ? kMaxParts : h);
 }
 
@@ -1366,16 +1377,16 @@ hipError_t launch_typed(const VerifyArgs& v, hipStream_t stream) {
     const int esize = Vec<DT>::kBytes;
     // draft-row features exist only where draft rows are read (stochastic)
     const bool feat = !GREEDY && (v.out_q_entropy != nullptr || v.out_q_max != nullptr);
+    const int parts = host_row_parts(v.vocab, GREEDY);
     Args a{static_cast<const char*>(v.target), v.target_ld * esize, v.target_rows,
            static_cast<const char*>(v.draft), v.draft_ld * esize, v.vocab, v.draft_tokens,
-           v.cu_rows, v.k_max, kLog2e / v.temperature, v.seed, v.step,
+           v.cu_rows, v.k_max, parts, kLog2e / v.temperature, v.seed, v.step,
            static_cast<PartStat*>(v.ws),
            reinterpret_cast<FeatPart*>(static_cast<char*>(v.ws) + stats_bytes(v.n_req, v.k_max)),
            v.out_tokens, v.out_accepted, v.out_p_draft, v.out_q_draft, v.out_residual_mass,
            v.out_q_entropy, v.out_q_max, v.dev_error};  // greedy: -1 written there
     const int slots = GREEDY ? v.k_max + 1 : 2 * v.k_max + 1;
     if (v.stages & 1) {
-        const int parts = host_row_parts(v.vocab);
         const dim3 grid((unsigned)((int64_t)v.n_req * slots * parts));  // < 2^23 (host-checked)
         if constexpr (GREEDY)
             hipLaunchKernelGGL((rowstats_kernel<DT, true, false>), grid, dim3(kGreedyThreads), 0, stream,

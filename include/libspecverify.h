@@ -314,10 +314,10 @@ sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
  *                row statistics and draft-row feature sums passed from the
  *                first launch to the second).  Calls that overlap in time
  *                must not share a workspace.
- * Launch: two kernels.  Pass 1: one workgroup (512 threads stochastic, 256
- * greedy) per candidate row part, rows cut into ceil(vocab / 131072) <= 8
- * parts (n_req * (2*k_max + 1) rows stochastic, n_req * (k_max + 1) greedy;
- * workgroups beyond the kept rows do nothing).  Pass 2: one workgroup per request (1024 threads
+ * Launch: two kernels.  Pass 1: one 512-thread workgroup per candidate row
+ * part, rows cut into ceil(vocab / 131072) <= 8 parts (n_req * (2*k_max + 1)
+ * rows stochastic, n_req * (k_max + 1) greedy; workgroups beyond the kept
+ * rows do nothing).  Pass 2: one workgroup per request (1024 threads
  * stochastic, 64 greedy) merges the parts, decides and draws.
  * Errors: SV_ERR_NULL; SV_ERR_DTYPE; SV_ERR_SHAPE if n_req < 0, k_max outside
  * [0, SV_MAX_DRAFT], n_req * (2*k_max + 1) > SV_MAX_VERIFY_SLOTS, vocab outside
