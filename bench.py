@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--separate-pack", action="store_true",
                     help="budget and pack as two calls (sv_budget_select, sv_pack_varlen) "
                          "instead of sv_budget_select_pack")
+    ap.add_argument("--legs", default="greedy,mix",
+                    help="secondary legs after the headline: greedy (same workload, greedy "
+                         "mode), mix (256 requests, K_r up to 15, V = 256000, fp32); 'none'")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only copy a device buffer of this many MiB three times and exit: "
                          "a plain copy of known size, to scale HBM byte counters by")
@@ -180,7 +183,10 @@ def cpu_baseline(args, w, tgt_full, drf_full, toks_np):
         rows1 += int(cu[-1])
     t1 = time.perf_counter() - t_c
 
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    # one worker process per CPU this process may run on, at most 16: the host
+    # CPUs allotted to a one-GPU job (more processes would compete for them)
+    host_cpus = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, host_cpus))
     _CPU.update(K=K, V=V, kept=kept, tgt=tgt_full, drf=drf_full, toks=toks_np, greedy=greedy,
                 omode=omode, tau=w.tau, seed=w.seed)
     chunks = min(n, 4 * workers)
@@ -200,7 +206,315 @@ def cpu_baseline(args, w, tgt_full, drf_full, toks_np):
             "sample": f"{steps2} whole steps of {args.workload} (budget and pack in the parent, "
                       f"{args.mode} verify of {rows_step} target rows each spread over {workers} "
                       f"worker processes, Philox step varied) with numpy fp64, {t2:.1f} s; on one "
-                      f"thread {steps1} steps in {t1:.1f} s = {rows1 / t1:.2f} rows/s"}
+                      f"thread {steps1} steps in {t1:.1f} s = {rows1 / t1:.2f} rows/s",
+            "single_thread_value": round(rows1 / t1, 2),
+            "host_cpus": host_cpus, "host_cpus_total": os.cpu_count(),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's guess."""
+    import platform
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+class Leg:
+    """Device state for timing one workload in one mode: inputs, outputs, the
+    workspaces, and `replicas` copies of the packed target rows and the draft
+    rows (reads then come from HBM, not the 256 MB Infinity Cache).  `share`
+    reuses another leg's logit replicas and budget (same workload, other mode)."""
+
+    def __init__(self, sv, torch, w, mode_name, tgt_full_d, drf_full_d, toks_np, args,
+                 share=None):
+        self.sv, self.torch, self.w, self.args = sv, torch, w, args
+        self.mode = sv.SV_GREEDY if mode_name == "greedy" else sv.SV_STOCHASTIC
+        self.mode_name = mode_name
+        dev = self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream()
+        n, K, V = w.n, w.k_max, w.vocab
+        self.esize = 2 if w.dtype == "bf16" else 4
+
+        def d(a, dtype=None):
+            t = torch.from_numpy(np.ascontiguousarray(a))
+            return (t.to(dtype) if dtype is not None else t).to(dev)
+
+        self.d = d
+        self.cost = sv.sv_cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
+        self.conf_d, self.dl_d, self.cost_d = d(w.conf), d(w.draft_len), d(self.cost)
+        self.last_d, self.toks_d = d(w.last_token), d(toks_np)
+        self.tgt_full_d, self.drf_full_d = tgt_full_d, drf_full_d
+        e = lambda *shape, dt=torch.int32: torch.empty(*shape, dtype=dt, device=dev)
+        self.kept, self.budget, self.err = e(n), e(1), torch.zeros(1, dtype=torch.int32, device=dev)
+        self.survival = e(n, K, dt=torch.float32)
+        self.cap = cap = n * (K + 1)
+        self.cu, self.row_req, self.row_pos, self.packed = e(n + 1), e(cap), e(cap), e(cap)
+        self.ws = torch.zeros(sv.sv_verify_workspace_bytes(n, K), dtype=torch.uint8, device=dev)
+        self.bws = torch.empty(max(1, sv.sv_budget_workspace_bytes(n, K)), dtype=torch.uint8,
+                               device=dev)
+        self.tok_out, self.acc_out = e(n, K + 1), e(n)
+        self.p_out, self.q_out = e(n, K, dt=torch.float32), e(n, K, dt=torch.float32)
+        self.res_out = e(n, dt=torch.float32)
+
+        # set-up pass: the budget's packing decides which target rows the (stand-in)
+        # target forward would produce; gather them once into packed buffers
+        sv.sv_budget_select(self.conf_d, self.dl_d, self.cost_d, w.t_base, w.n_bonus, self.kept,
+                            self.budget, self.survival, self.err, ws=self.bws)
+        sv.sv_pack_varlen(self.kept, self.last_d, self.toks_d, self.cu, self.row_req,
+                          self.row_pos, self.packed, self.err)
+        torch.cuda.synchronize()
+        self.kept_h = self.kept.cpu().numpy()
+        self.B = int(self.budget.item())
+        self.rows_t = int(self.cu[-1].item())
+        self.rows_d = int(self.kept_h.sum())
+        if share is not None:
+            self.replicas = share.replicas
+        else:
+            idx = np.concatenate([r * (K + 1) + np.arange(int(self.kept_h[r]) + 1)
+                                  for r in range(n)])
+            idx_d = d(idx.astype(np.int64))
+            self.replicas = []
+            for i in range(args.replicas):
+                tp = torch.full((cap, V), float("nan"), dtype=tgt_full_d.dtype, device=dev)
+                tp[: self.rows_t] = tgt_full_d.index_select(0, idx_d)
+                dr = drf_full_d if i == 0 else drf_full_d.clone()
+                self.replicas.append((tp, dr))
+        torch.cuda.synchronize()
+
+    def step(self, i, events=None, reps=None, cu_rows=None, kept_in=None):
+        """One step; events (5) bracket budget, pack, verify pass 1, verify pass 2."""
+        sv, w = self.sv, self.w
+        tp, dr = (reps or self.replicas)[i % len(reps or self.replicas)]
+        cu_i = self.cu if cu_rows is None else cu_rows
+
+        def mark(k):
+            if events is not None:
+                events[k].record(self.stream)
+
+        mark(0)
+        if kept_in is None and self.args.separate_pack:
+            sv.sv_budget_select(self.conf_d, self.dl_d, self.cost_d, w.t_base, w.n_bonus,
+                                self.kept, self.budget, self.survival, self.err, ws=self.bws)
+            mark(1)
+            sv.sv_pack_varlen(self.kept, self.last_d, self.toks_d, self.cu, self.row_req,
+                              self.row_pos, self.packed, self.err)
+        elif kept_in is None:  # budget and pack in one launch fewer
+            sv.sv_budget_select_pack(self.conf_d, self.dl_d, self.cost_d, w.t_base, w.n_bonus,
+                                     self.last_d, self.toks_d, self.kept, self.budget, self.cu,
+                                     self.row_req, self.row_pos, self.packed, self.survival,
+                                     self.err, ws=self.bws)
+            mark(1)
+        else:
+            mark(1)
+        mark(2)
+        for stage in (1, 2):
+            sv.sv_verify_stages(tp, dr, self.toks_d, cu_i, self.mode, w.tau, w.seed, i,
+                                self.tok_out, self.acc_out, self.ws, stage, self.p_out,
+                                self.q_out, self.res_out, self.err, vocab=w.vocab)
+            mark(2 + stage)
+
+    def pass2_rows(self, steps, kept_h_, **kw):
+        """Rows the draws re-read in each of `steps` (deterministic: same step index,
+        same draws): two per rejected request, one per request that accepted all."""
+        if self.mode == self.sv.SV_GREEDY:
+            return np.zeros(len(steps))
+        out = []
+        n = self.w.n
+        for i in steps:
+            self.step(i, **kw)
+            acc = self.acc_out.cpu().numpy()
+            rej = int(((acc >= 0) & (acc < kept_h_)).sum())
+            out.append(2 * rej + (n - rej))
+        return np.array(out, dtype=np.float64)
+
+    def timed(self, iters, **kw):
+        torch = self.torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(iters)]
+        torch.cuda.synchronize()
+        t0_ = time.perf_counter()
+        for i in range(iters):
+            self.step(i, ev[i], **kw)
+        torch.cuda.synchronize()
+        wall_ = time.perf_counter() - t0_
+        ms = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(4)]
+                       for i in range(iters)])
+        if int(self.err.item()) != 0:
+            raise RuntimeError(f"device error bits {int(self.err.item())} during the benchmark")
+        return wall_, ms
+
+    def pass1_launch_ms(self, iters, reps=None, cu_rows=None, features=False):
+        """Mean duration of the roofline kernel: `iters` pass-1 launches back to
+        back (replicas in turn) between two events on the launch stream.
+        features: the launch that also accumulates the draft-row features."""
+        sv, torch, w = self.sv, self.torch, self.w
+        reps = reps or self.replicas
+        cu_i = self.cu if cu_rows is None else cu_rows
+        fkw = {}
+        if features:
+            fkw = dict(out_q_entropy=torch.empty(w.n, w.k_max, dtype=torch.float32,
+                                                 device=self.dev),
+                       out_q_max=torch.empty(w.n, w.k_max, dtype=torch.float32,
+                                             device=self.dev))
+        for i in range(2):
+            tp_, dr_ = reps[i % len(reps)]
+            sv.sv_verify_stages(tp_, dr_, self.toks_d, cu_i, self.mode, w.tau, w.seed, i,
+                                self.tok_out, self.acc_out, self.ws, 1, self.p_out, self.q_out,
+                                self.res_out, self.err, vocab=w.vocab, **fkw)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(iters):
+            tp_, dr_ = reps[i % len(reps)]
+            sv.sv_verify_stages(tp_, dr_, self.toks_d, cu_i, self.mode, w.tau, w.seed, i,
+                                self.tok_out, self.acc_out, self.ws, 1, self.p_out, self.q_out,
+                                self.res_out, self.err, vocab=w.vocab, **fkw)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    def full_k_inputs(self):
+        """Every draft kept: request r's rows 0..K_r packed at cu_full[r] (the layout a
+        varlen target forward writes), gathered from the per-request stride K+1."""
+        sv, torch, w = self.sv, self.torch, self.w
+        n, K = w.n, w.k_max
+        cu_full = torch.empty(n + 1, dtype=torch.int32, device=self.dev)
+        sv.sv_pack_varlen(self.dl_d, self.last_d, self.toks_d, cu_full, self.row_req,
+                          self.row_pos, self.packed, self.err)
+        full_idx = np.concatenate([r * (K + 1) + np.arange(int(w.draft_len[r]) + 1)
+                                   for r in range(n)])
+        tgt_packed = self.tgt_full_d.index_select(0, self.d(full_idx.astype(np.int64)))
+        reps = [(tgt_packed if i == 0 else tgt_packed.clone(), self.replicas[i][1])
+                for i in range(len(self.replicas))]
+        rows_tf = int(cu_full[-1].item())
+        rows_df = int(w.draft_len.sum()) if self.mode == sv.SV_STOCHASTIC else 0
+        return reps, cu_full, rows_tf, rows_df
+
+    def pass1_bytes(self, rows_t, rows_d):
+        rd = rows_d if self.mode == self.sv.SV_STOCHASTIC else 0
+        return (rows_t + rd) * self.w.vocab * self.esize
+
+    def leg_figures(self, steps, full_k_iters):
+        """The figures reported for a secondary leg: eager steps back to back, the
+        staged loop, pass 1 back to back (adaptive and full K), pass 2's bytes."""
+        run = lambda i: self.step(i)
+        for i in range(3):
+            self.step(i)
+        wall = timed_plain(self.torch, steps, run)
+        for i in range(2):
+            self.step(i)
+        _, stage_ms = self.timed(steps)
+        p2_rows = self.pass2_rows(range(steps), self.kept_h)
+        p1_ms = self.pass1_launch_ms(steps)
+        p1_bytes = self.pass1_bytes(self.rows_t, self.rows_d)
+        p2_bytes = float(np.mean(p2_rows)) * self.w.vocab * self.esize
+        p2_ms = float(np.mean(stage_ms[:, 3]))
+        out = {
+            "workload": self.w.name, "mode": self.mode_name, "logits": self.w.dtype,
+            "temperature": self.w.tau, "budget": self.B, "target_rows": self.rows_t,
+            "draft_rows": self.rows_d if self.mode == self.sv.SV_STOCHASTIC else 0,
+            "step_us": round(wall * 1e6 / steps, 2),
+            "rows_per_s": round(self.rows_t / (wall / steps), 1),
+            "budget_pack_us": round(float(np.mean(stage_ms[:, 0] + stage_ms[:, 1])) * 1e3, 2),
+            "pass1_us": round(p1_ms * 1e3, 2), "pass1_bytes": int(p1_bytes),
+            "pass1_gbps": round(p1_bytes / (p1_ms * 1e-3) / 1e9, 1),
+            "pass1_frac": round(p1_bytes / (p1_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "pass2_us": round(p2_ms * 1e3, 2), "pass2_bytes": int(p2_bytes),
+        }
+        if p2_bytes > 0:
+            out["pass2_gbps"] = round(p2_bytes / (p2_ms * 1e-3) / 1e9, 1)
+            out["pass2_frac"] = round(p2_bytes / (p2_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        if full_k_iters > 0:
+            reps, cu_full, rows_tf, rows_df = self.full_k_inputs()
+            f_ms = self.pass1_launch_ms(full_k_iters, reps=reps, cu_rows=cu_full)
+            f_bytes = self.pass1_bytes(rows_tf, rows_df)
+            out["full_k"] = {"target_rows": rows_tf, "draft_rows": rows_df,
+                             "pass1_us": round(f_ms * 1e3, 2), "pass1_bytes": int(f_bytes),
+                             "pass1_gbps": round(f_bytes / (f_ms * 1e-3) / 1e9, 1),
+                             "pass1_frac": round(f_bytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                                 4)}
+        return out
+
+
+def timed_plain(torch, iters, fn):
+    """Wall time of `iters` calls of fn with nothing else on the stream."""
+    torch.cuda.synchronize()
+    t0_ = time.perf_counter()
+    for i in range(iters):
+        fn(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0_
+
+
+def graph_us(torch, fn, iters):
+    """GPU time per call of a small entry point: `iters` calls captured in one
+    HIP graph and replayed between two events, so the figure is the kernels'
+    own time back to back, not the host's per-call binding overhead (which
+    exceeds these kernels' few microseconds when they are launched from
+    Python one by one)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(iters):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_.record(cur)
+    g.replay()
+    b_.record(cur)
+    torch.cuda.synchronize()
+    return round(a_.elapsed_time(b_) / iters * 1e3, 2)
+
+
+def generate_host(w):
+    """Full logits of every request on the host: target row (r, j) at r*(K+1) + j,
+    draft row (r, j) at r*K + j (NaN elsewhere), and both modes' draft ids."""
+    n, K, V = w.n, w.k_max, w.vocab
+    tgt_full = np.full((n * (K + 1), V), np.nan, dtype=np.float32)
+    drf_full = np.full((n * K, V), np.nan, dtype=np.float32)
+    toks = {m: np.full((n, K), -1, dtype=np.int32) for m in ("stochastic", "greedy")}
+    for r in range(n):
+        rq = w.request(r)
+        Kr = int(w.draft_len[r])
+        tgt_full[r * (K + 1): r * (K + 1) + Kr + 1] = rq["target"]
+        drf_full[r * K: r * K + Kr] = rq["draft"]
+        toks["stochastic"][r] = rq["tok_stochastic"]
+        toks["greedy"][r] = rq["tok_greedy"]
+        w.drop_cache()
+    return tgt_full, drf_full, toks
+
+
+def generate_device(torch, w, ldt):
+    """The same layout as generate_host, written to the device request by request
+    (the large workloads never sit whole in host memory); padding rows are NaN."""
+    n, K, V = w.n, w.k_max, w.vocab
+    dev = torch.device("cuda:0")
+    tgt = torch.full((n * (K + 1), V), float("nan"), dtype=ldt, device=dev)
+    drf = torch.full((n * K, V), float("nan"), dtype=ldt, device=dev)
+    toks = {m: np.full((n, K), -1, dtype=np.int32) for m in ("stochastic", "greedy")}
+    for r in range(n):
+        rq = w.request(r)
+        Kr = int(w.draft_len[r])
+        tgt[r * (K + 1): r * (K + 1) + Kr + 1] = torch.from_numpy(rq["target"]).to(dev, ldt)
+        if Kr:
+            drf[r * K: r * K + Kr] = torch.from_numpy(rq["draft"]).to(dev, ldt)
+        toks["stochastic"][r] = rq["tok_stochastic"]
+        toks["greedy"][r] = rq["tok_greedy"]
+        w.drop_cache()
+    torch.cuda.synchronize()
+    return tgt, drf, toks
 
 
 def main():
@@ -221,24 +535,12 @@ def main():
     import workloads
 
     w = workloads.make(args.workload)
-    mode = sv.SV_GREEDY if args.mode == "greedy" else sv.SV_STOCHASTIC
     ldt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    esize = 2 if w.dtype == "bf16" else 4
     n, K, V = w.n, w.k_max, w.vocab
 
     t0 = time.time()
-    # full logits: target row (r, j) at r*(K+1) + j, draft row (r, j) at r*K + j
-    tgt_full = np.full((n * (K + 1), V), np.nan, dtype=np.float32)
-    drf_full = np.full((n * K, V), np.nan, dtype=np.float32)
-    tok_key = "tok_greedy" if args.mode == "greedy" else "tok_stochastic"
-    toks_np = np.full((n, K), -1, dtype=np.int32)
-    for r in range(n):
-        rq = w.request(r)
-        Kr = int(w.draft_len[r])
-        tgt_full[r * (K + 1): r * (K + 1) + Kr + 1] = rq["target"]
-        drf_full[r * K: r * K + Kr] = rq["draft"]
-        toks_np[r] = rq[tok_key]
-        w.drop_cache()
+    tgt_full, drf_full, toks_all = generate_host(w)
+    toks_np = toks_all[args.mode]
     print(f"[bench] generated {args.workload} in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
 
@@ -251,120 +553,18 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
 
     def d(a, dtype=None):
         t = torch.from_numpy(np.ascontiguousarray(a))
         return (t.to(dtype) if dtype is not None else t).to(dev)
 
-    cost = sv.sv_cost_table_prepare(w.raw_cost, w.granule, w.cost_len)
-    conf_d, dl_d, cost_d = d(w.conf), d(w.draft_len), d(cost)
-    last_d, toks_d = d(w.last_token), d(toks_np)
     tgt_full_d = d(tgt_full, ldt)
     drf_full_d = d(drf_full, ldt)
-
-    # outputs and workspace, allocated once
-    kept = torch.empty(n, dtype=torch.int32, device=dev)
-    budget = torch.empty(1, dtype=torch.int32, device=dev)
-    survival = torch.empty(n, K, dtype=torch.float32, device=dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    cap = n * (K + 1)
-    cu = torch.empty(n + 1, dtype=torch.int32, device=dev)
-    row_req = torch.empty(cap, dtype=torch.int32, device=dev)
-    row_pos = torch.empty(cap, dtype=torch.int32, device=dev)
-    packed = torch.empty(cap, dtype=torch.int32, device=dev)
-    ws = torch.zeros(sv.sv_verify_workspace_bytes(n, K), dtype=torch.uint8, device=dev)
-    bws = torch.empty(max(1, sv.sv_budget_workspace_bytes(n, K)), dtype=torch.uint8, device=dev)
-    tok_out = torch.empty(n, K + 1, dtype=torch.int32, device=dev)
-    acc_out = torch.empty(n, dtype=torch.int32, device=dev)
-    p_out = torch.empty(n, K, dtype=torch.float32, device=dev)
-    q_out = torch.empty(n, K, dtype=torch.float32, device=dev)
-    res_out = torch.empty(n, dtype=torch.float32, device=dev)
-
-    # set-up pass: the budget's packing decides which target rows the (stand-in)
-    # target forward would produce; gather them once into packed buffers
-    sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, kept, budget, survival, err,
-                        ws=bws)
-    sv.sv_pack_varlen(kept, last_d, toks_d, cu, row_req, row_pos, packed, err)
-    torch.cuda.synchronize()
-    kept_h = kept.cpu().numpy()
-    cu_h = cu.cpu().numpy()
-    B = int(budget.item())
-    rows_t = int(cu_h[-1])
-    rows_d = int(kept_h.sum())
-    idx = np.concatenate([r * (K + 1) + np.arange(int(kept_h[r]) + 1) for r in range(n)])
-    idx_d = d(idx.astype(np.int64))
-    replicas = []
-    for i in range(args.replicas):
-        tp = torch.full((cap, V), float("nan"), dtype=ldt, device=dev)
-        tp[:rows_t] = tgt_full_d.index_select(0, idx_d)
-        dr = drf_full_d if i == 0 else drf_full_d.clone()
-        replicas.append((tp, dr))
-    torch.cuda.synchronize()
-
-    def step(i, events=None, reps=None, cu_rows=None, kept_in=None):
-        """One step; events (5) bracket budget, pack, verify pass 1, verify pass 2."""
-        tp, dr = (reps or replicas)[i % len(reps or replicas)]
-        cu_i = cu if cu_rows is None else cu_rows
-
-        def mark(k):
-            if events is not None:
-                events[k].record(stream)
-
-        mark(0)
-        if kept_in is None and args.separate_pack:
-            sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, kept, budget,
-                                survival, err, ws=bws)
-            mark(1)
-            sv.sv_pack_varlen(kept, last_d, toks_d, cu, row_req, row_pos, packed, err)
-        elif kept_in is None:  # budget and pack in one launch fewer
-            sv.sv_budget_select_pack(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, last_d, toks_d,
-                                     kept, budget, cu, row_req, row_pos, packed, survival, err,
-                                     ws=bws)
-            mark(1)
-        else:
-            mark(1)
-        mark(2)
-        for stage in (1, 2):
-            sv.sv_verify_stages(tp, dr, toks_d, cu_i, mode, w.tau, w.seed, i, tok_out, acc_out,
-                                ws, stage, p_out, q_out, res_out, err, vocab=V)
-            mark(2 + stage)
-
-    def pass2_rows(steps, kept_h_, **kw):
-        """Rows the draws re-read in each of `steps` (deterministic: same step index,
-        same draws): two per rejected request, one per request that accepted all."""
-        if mode == sv.SV_GREEDY:
-            return np.zeros(len(steps))
-        out = []
-        for i in steps:
-            step(i, **kw)
-            acc = acc_out.cpu().numpy()
-            rej = int(((acc >= 0) & (acc < kept_h_)).sum())
-            out.append(2 * rej + (n - rej))
-        return np.array(out, dtype=np.float64)
-
-    def timed(iters, **kw):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(iters)]
-        torch.cuda.synchronize()
-        t0_ = time.perf_counter()
-        for i in range(iters):
-            step(i, ev[i], **kw)
-        torch.cuda.synchronize()
-        wall_ = time.perf_counter() - t0_
-        ms = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(4)]
-                       for i in range(iters)])
-        if int(err.item()) != 0:
-            raise RuntimeError(f"device error bits {int(err.item())} during the benchmark")
-        return wall_, ms
-
-    def timed_plain(iters, fn):
-        """Wall time of `iters` steps with nothing else on the stream."""
-        torch.cuda.synchronize()
-        t0_ = time.perf_counter()
-        for i in range(iters):
-            fn(i)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0_
+    del tgt_full, drf_full
+    leg = Leg(sv, torch, w, args.mode, tgt_full_d, drf_full_d, toks_np, args)
+    mode = leg.mode
+    rows_t, rows_d, B = leg.rows_t, leg.rows_d, leg.B
+    esize = leg.esize
 
     # the headline: K steps back to back, launched eagerly or replayed from HIP
     # graphs (one per replica and Philox step, cycled)
@@ -374,13 +574,13 @@ def main():
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for i in range(2):
-                step(i)
+                leg.step(i)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         for i in range(args.graphs):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(i)
+                leg.step(i)
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -388,129 +588,73 @@ def main():
         if graphs:
             graphs[i % len(graphs)].replay()
         else:
-            step(i)
+            leg.step(i)
 
     for i in range(args.warmup):
         run_step(i)
-    wall = timed_plain(args.steps, run_step)
-    wall_eager = timed_plain(args.steps, step) if graphs else wall
+    wall = timed_plain(torch, args.steps, run_step)
+    wall_eager = timed_plain(torch, args.steps, leg.step) if graphs else wall
     # per-stage times in a separate loop (events between stages cost time)
     for i in range(2):
-        step(i)
-    _, stage_ms = timed(args.steps)
-    p2_rows = pass2_rows(range(args.steps), kept_h)
-
-    def pass1_launch_ms(iters, reps=None, cu_rows=None, features=False):
-        """Mean duration of the roofline kernel: `iters` pass-1 launches back to
-        back (replicas alternating) between two events on the launch stream.
-        features: the launch that also accumulates the draft-row features."""
-        reps = reps or replicas
-        cu_i = cu if cu_rows is None else cu_rows
-        fkw = {}
-        if features:
-            fkw = dict(out_q_entropy=torch.empty(n, K, dtype=torch.float32, device=dev),
-                       out_q_max=torch.empty(n, K, dtype=torch.float32, device=dev))
-        for i in range(2):
-            tp_, dr_ = reps[i % len(reps)]
-            sv.sv_verify_stages(tp_, dr_, toks_d, cu_i, mode, w.tau, w.seed, i, tok_out,
-                                acc_out, ws, 1, p_out, q_out, res_out, err, vocab=V, **fkw)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(iters):
-            tp_, dr_ = reps[i % len(reps)]
-            sv.sv_verify_stages(tp_, dr_, toks_d, cu_i, mode, w.tau, w.seed, i, tok_out,
-                                acc_out, ws, 1, p_out, q_out, res_out, err, vocab=V, **fkw)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / iters
-
-    def graph_us(fn, iters):
-        """GPU time per call of a small entry point: `iters` calls captured in one
-        HIP graph and replayed between two events, so the figure is the kernels'
-        own time back to back, not the host's per-call binding overhead (which
-        exceeds these kernels' few microseconds when they are launched from
-        Python one by one)."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for _ in range(3):
-                fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(iters):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        cur = torch.cuda.current_stream()
-        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a_.record(cur)
-        g.replay()
-        b_.record(cur)
-        torch.cuda.synchronize()
-        return round(a_.elapsed_time(b_) / iters * 1e3, 2)
+        leg.step(i)
+    _, stage_ms = leg.timed(args.steps)
+    p2_rows = leg.pass2_rows(range(args.steps), leg.kept_h)
 
     ms_per_step = wall * 1e3 / args.steps
     pass1_ms, pass2_ms = float(np.mean(stage_ms[:, 2])), float(np.mean(stage_ms[:, 3]))
-    roof_ms = pass1_launch_ms(args.steps)
-    pass1_bytes = (rows_t + (rows_d if mode == sv.SV_STOCHASTIC else 0)) * V * esize
+    roof_ms = leg.pass1_launch_ms(args.steps)
+    pass1_bytes = leg.pass1_bytes(rows_t, rows_d)
     pass2_bytes = float(np.mean(p2_rows)) * V * esize
     achieved = pass1_bytes / (roof_ms * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- full K leg
     full = None
     if args.full_k_iters > 0:
-        cu_full = torch.empty(n + 1, dtype=torch.int32, device=dev)
-        sv.sv_pack_varlen(dl_d, last_d, toks_d, cu_full, row_req, row_pos, packed, err)
-        # every draft kept: request r's rows 0..K_r packed at cu_full[r] (the layout a
-        # varlen target forward writes), gathered from the per-request stride K+1
-        full_idx = np.concatenate([r * (K + 1) + np.arange(int(w.draft_len[r]) + 1)
-                                   for r in range(n)])
-        tgt_packed = tgt_full_d.index_select(0, d(full_idx.astype(np.int64)))
-        full_reps = [(tgt_packed if i == 0 else tgt_packed.clone(), replicas[i][1])
-                     for i in range(args.replicas)]
-        rows_tf = int(cu_full[-1].item())
-        rows_df = int(w.draft_len.sum())
+        full_reps, cu_full, rows_tf, rows_df = leg.full_k_inputs()
         kw = dict(reps=full_reps, cu_rows=cu_full, kept_in=True)
         for i in range(3):
-            step(i, **kw)
-        _, fms = timed(args.full_k_iters, **kw)
+            leg.step(i, **kw)
+        _, fms = leg.timed(args.full_k_iters, **kw)
         f1, f2 = float(np.mean(fms[:, 2])), float(np.mean(fms[:, 3]))
-        f_p1 = (rows_tf + (rows_df if mode == sv.SV_STOCHASTIC else 0)) * V * esize
-        f_p2 = float(np.mean(pass2_rows(range(args.full_k_iters), w.draft_len, **kw))) * V * esize
+        f_p1 = leg.pass1_bytes(rows_tf, rows_df)
+        f_p2 = float(np.mean(leg.pass2_rows(range(args.full_k_iters), w.draft_len, **kw))) \
+            * V * esize
+        f1_launch = leg.pass1_launch_ms(args.full_k_iters, reps=full_reps, cu_rows=cu_full)
         full = {
-            "target_rows": rows_tf, "draft_rows": rows_df if mode == sv.SV_STOCHASTIC else 0,
+            "target_rows": rows_tf, "draft_rows": rows_df,
             "pass1_us": round(f1 * 1e3, 2), "pass2_us": round(f2 * 1e3, 2),
+            "pass1_launch_us": round(f1_launch * 1e3, 2),
             "pass1_bytes": int(f_p1), "pass2_bytes": int(f_p2),
-            "pass1_gbps": round(f_p1 / (f1 * 1e-3) / 1e9, 1),
-            "pass1_frac": round(f_p1 / (f1 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "pass1_gbps": round(f_p1 / (f1_launch * 1e-3) / 1e9, 1),
+            "pass1_frac": round(f_p1 / (f1_launch * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "pass2_gbps": round(f_p2 / (f2 * 1e-3) / 1e9, 1) if f_p2 else None,
             "verify_gbps": round((f_p1 + f_p2) / ((f1 + f2) * 1e-3) / 1e9, 1),
             "verify_frac": round((f_p1 + f_p2) / ((f1 + f2) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "verify_rows_per_s": round(rows_tf / ((f1 + f2) * 1e-3), 1),
             "iters": args.full_k_iters,
         }
+        del full_reps
 
     # -------------------------------------------- draft-row features leg
     # pass 1 asked for the draft rows' entropy and largest probability as well
     features = None
     if mode == sv.SV_STOCHASTIC:
-        feat_ms = pass1_launch_ms(args.steps, features=True)
+        feat_ms = leg.pass1_launch_ms(args.steps, features=True)
         features = {"pass1_us": round(feat_ms * 1e3, 2),
                     "pass1_gbps": round(pass1_bytes / (feat_ms * 1e-3) / 1e9, 1),
                     "vs_plain_pass1": round(feat_ms / roof_ms, 4)}
 
     # ------------------------------------------------ uniform draft length leg
     # the DSD-style alternative to the adaptive budget: one K for the batch
+    conf_d, dl_d, cost_d, last_d, toks_d = leg.conf_d, leg.dl_d, leg.cost_d, leg.last_d, leg.toks_d
+    err, bws, cap = leg.err, leg.bws, leg.cap
     uk_k = torch.empty(1, dtype=torch.int32, device=dev)
     uk_kept = torch.empty(n, dtype=torch.int32, device=dev)
-    uk_us = graph_us(lambda: sv.sv_uniform_k_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus,
-                                                    uk_kept, uk_k, None, err), args.steps)
+    uk_us = graph_us(torch, lambda: sv.sv_uniform_k_select(conf_d, dl_d, cost_d, w.t_base,
+                                                           w.n_bonus, uk_kept, uk_k, None, err),
+                     args.steps)
     uniform_k = {"us": uk_us, "k": int(uk_k.item()), "drafts_verified": int(uk_kept.sum().item())}
 
-    # ----------------------------------------- stale-confidence budget leg
-    # the pipeline that sizes B one step ahead: the step itself only allocates
-    # the slots of a B already in device memory (here the budget selected above)
     # the step's budget and pack call on its own, graph-replayed: its kernels'
     # time without the staged loop's events around it
     bs_kept = torch.empty(n, dtype=torch.int32, device=dev)
@@ -518,14 +662,19 @@ def main():
     bs_cu = torch.empty(n + 1, dtype=torch.int32, device=dev)
     bs_maps = [torch.empty(cap, dtype=torch.int32, device=dev) for _ in range(3)]
     budget_select_graph_us = graph_us(
+        torch,
         lambda: sv.sv_budget_select_pack(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, last_d,
                                          toks_d, bs_kept, bs_budget, bs_cu, *bs_maps, None, err,
                                          ws=bws),
         args.steps)
 
+    # ----------------------------------------- stale-confidence budget leg
+    # the pipeline that sizes B one step ahead: the step itself only allocates
+    # the slots of a B already in device memory (here the budget selected above)
     al_kept = torch.empty(n, dtype=torch.int32, device=dev)
     budget_allocate_us = graph_us(
-        lambda: sv.sv_budget_allocate(conf_d, dl_d, budget, al_kept, None, None, err, ws=bws),
+        torch, lambda: sv.sv_budget_allocate(conf_d, dl_d, leg.budget, al_kept, None, None, err,
+                                             ws=bws),
         args.steps)
 
     # ------------------------------------------ acceptance statistics and calibration leg
@@ -535,25 +684,56 @@ def main():
     if mode == sv.SV_STOCHASTIC:
         qh = torch.empty(n, K, dtype=torch.float32, device=dev)
         qm = torch.empty(n, K, dtype=torch.float32, device=dev)
-        tp0, dr0 = replicas[0]
-        sv.sv_verify_stages(tp0, dr0, toks_d, cu, mode, w.tau, w.seed, 0, tok_out, acc_out, ws, 3,
-                            p_out, q_out, res_out, err, vocab=V, out_q_entropy=qh, out_q_max=qm)
+        tp0, dr0 = leg.replicas[0]
+        sv.sv_verify_stages(tp0, dr0, toks_d, leg.cu, mode, w.tau, w.seed, 0, leg.tok_out,
+                            leg.acc_out, leg.ws, 3, leg.p_out, leg.q_out, leg.res_out, err,
+                            vocab=V, out_q_entropy=qh, out_q_max=qm)
         attempted = torch.zeros(K, dtype=torch.int64, device=dev)
         accepted_at = torch.zeros(K, dtype=torch.int64, device=dev)
         totals = torch.zeros(2, dtype=torch.int64, device=dev)
         theta = torch.zeros(K + 3, dtype=torch.float32, device=dev)
         pred = torch.empty(n, K, dtype=torch.float32, device=dev)
         legs = {
-            "accept_stats_us": lambda: sv.sv_accept_stats(acc_out, cu, attempted, accepted_at,
-                                                          totals),
+            "accept_stats_us": lambda: sv.sv_accept_stats(leg.acc_out, leg.cu, attempted,
+                                                          accepted_at, totals),
             "calibrate_update_us": lambda: sv.sv_calibrate_update(
-                theta, q_out, acc_out, cu, 1e-3, q_entropy=qh, q_max=qm),
+                theta, leg.q_out, leg.acc_out, leg.cu, 1e-3, q_entropy=qh, q_max=qm),
             "calibrate_predict_us": lambda: sv.sv_calibrate_predict(
-                theta, q_out, pred, q_entropy=qh, q_max=qm),
+                theta, leg.q_out, pred, q_entropy=qh, q_max=qm),
         }
-        calibration = {key: graph_us(fn, args.steps) for key, fn in legs.items()}
+        calibration = {key: graph_us(torch, fn, args.steps) for key, fn in legs.items()}
 
-    # ------------------------------------------------------------ CPU oracle leg
+    # ---------------------------------- greedy mode on the same workload
+    # (same logit replicas and budget; the drafter's argmax ids; pass 1 reads
+    # the target rows only and pass 2 draws nothing)
+    wanted = set(x for x in args.legs.split(",") if x and x != "none")
+    greedy = None
+    if "greedy" in wanted and mode == sv.SV_STOCHASTIC:
+        gleg = Leg(sv, torch, w, "greedy", tgt_full_d, drf_full_d, toks_all["greedy"], args,
+                   share=leg)
+        greedy = gleg.leg_figures(args.steps, args.full_k_iters)
+        del gleg
+        print(f"[bench] greedy leg: {greedy['step_us']} us/step", file=sys.stderr, flush=True)
+
+    # ----------------------------- the mixed-length fp32 workload (V = 256,000)
+    mix = None
+    if "mix" in wanted:
+        del leg.replicas, tgt_full_d, drf_full_d
+        torch.cuda.empty_cache()
+        t1 = time.time()
+        wm = workloads.make("b256_mix_v256000")
+        mldt = torch.bfloat16 if wm.dtype == "bf16" else torch.float32
+        mt, md, mtoks = generate_device(torch, wm, mldt)
+        print(f"[bench] generated {wm.name} in {time.time() - t1:.1f}s", file=sys.stderr,
+              flush=True)
+        mleg = Leg(sv, torch, wm, "stochastic", mt, md, mtoks["stochastic"], args)
+        del mt, md
+        mix = mleg.leg_figures(max(10, args.steps // 4), max(10, args.full_k_iters // 4)
+                               if args.full_k_iters > 0 else 0)
+        del mleg
+        torch.cuda.empty_cache()
+        print(f"[bench] mixed leg: {mix['step_us']} us/step", file=sys.stderr, flush=True)
+
     traffic = measured_traffic(args.workload, args.mode)
     out = {
         "metric": METRIC,
@@ -587,6 +767,8 @@ def main():
         "verify_pass1_us": round(pass1_ms * 1e3, 2),
         "verify_pass2_us": round(pass2_ms * 1e3, 2),
         "verify_pass2_bytes": int(pass2_bytes),
+        "verify_pass2_frac": (round(pass2_bytes / (pass2_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+                              if pass2_bytes else None),
         "gpu_step_us": round(float(np.mean(stage_ms.sum(axis=1))) * 1e3, 2),
         "launch": "hip-graph replay" if graphs else "eager",
         "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 4),
@@ -595,6 +777,8 @@ def main():
         "calibration": calibration,
         "draft_features": features,
         "full_k": full,
+        "greedy": greedy,
+        "mix_v256000": mix,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
