@@ -77,6 +77,10 @@ def parse():
     ap.add_argument("--separate-pack", action="store_true",
                     help="budget and pack as two calls (sv_budget_select, sv_pack_varlen) "
                          "instead of sv_budget_select_pack")
+    ap.add_argument("--all-drafts", action="store_true",
+                    help="the timed step verifies every draft (full K) of the workload; budget "
+                         "and pack still run in the step, but verify reads the full-K packing "
+                         "(for profiling the largest size on its own)")
     ap.add_argument("--legs", default="greedy,mix",
                     help="secondary legs after the headline: greedy (same workload, greedy "
                          "mode), mix (256 requests, K_r up to 15, V = 256000, fp32); 'none'")
@@ -255,6 +259,7 @@ class Leg:
         self.survival = e(n, K, dt=torch.float32)
         self.cap = cap = n * (K + 1)
         self.cu, self.row_req, self.row_pos, self.packed = e(n + 1), e(cap), e(cap), e(cap)
+        self.verify_cu = self.cu  # the packing verify reads (the step's own by default)
         self.ws = torch.zeros(sv.sv_verify_workspace_bytes(n, K), dtype=torch.uint8, device=dev)
         self.bws = torch.empty(max(1, sv.sv_budget_workspace_bytes(n, K)), dtype=torch.uint8,
                                device=dev)
@@ -291,7 +296,7 @@ class Leg:
         """One step; events (5) bracket budget, pack, verify pass 1, verify pass 2."""
         sv, w = self.sv, self.w
         tp, dr = (reps or self.replicas)[i % len(reps or self.replicas)]
-        cu_i = self.cu if cu_rows is None else cu_rows
+        cu_i = self.verify_cu if cu_rows is None else cu_rows
 
         def mark(k):
             if events is not None:
@@ -354,7 +359,7 @@ class Leg:
         features: the launch that also accumulates the draft-row features."""
         sv, torch, w = self.sv, self.torch, self.w
         reps = reps or self.replicas
-        cu_i = self.cu if cu_rows is None else cu_rows
+        cu_i = self.verify_cu if cu_rows is None else cu_rows
         fkw = {}
         if features:
             fkw = dict(out_q_entropy=torch.empty(w.n, w.k_max, dtype=torch.float32,
@@ -562,6 +567,12 @@ def main():
     drf_full_d = d(drf_full, ldt)
     del tgt_full, drf_full
     leg = Leg(sv, torch, w, args.mode, tgt_full_d, drf_full_d, toks_np, args)
+    if args.all_drafts:
+        # verify reads every draft's rows; the step's budget and pack still run
+        reps_all, cu_all, rows_ta, rows_da = leg.full_k_inputs()
+        leg.replicas, leg.verify_cu = reps_all, cu_all
+        leg.rows_t, leg.rows_d, leg.B = rows_ta, int(w.draft_len.sum()), int(w.draft_len.sum())
+        leg.kept_h = w.draft_len.copy()
     mode = leg.mode
     rows_t, rows_d, B = leg.rows_t, leg.rows_d, leg.B
     esize = leg.esize
@@ -734,7 +745,7 @@ def main():
         torch.cuda.empty_cache()
         print(f"[bench] mixed leg: {mix['step_us']} us/step", file=sys.stderr, flush=True)
 
-    traffic = measured_traffic(args.workload, args.mode)
+    traffic = None if args.all_drafts else measured_traffic(args.workload, args.mode)
     out = {
         "metric": METRIC,
         "value": round(rows_t / (ms_per_step * 1e-3), 1),
@@ -752,7 +763,7 @@ def main():
             "workload": args.workload, "n_req": n, "k": K, "vocab": V,
             "logits": w.dtype, "mode": args.mode, "temperature": w.tau,
             "budget": B, "target_rows": rows_t, "draft_rows": rows_d,
-            "cost_granule": w.granule,
+            "cost_granule": w.granule, "drafts": "all" if args.all_drafts else "adaptive",
         },
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
