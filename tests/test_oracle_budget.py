@@ -123,6 +123,72 @@ def test_confidence_sign_is_dropped():
                                            dtype=np.uint32))
     assert oracle.clamp_confidence(np.float32(2.0 ** -149)) == np.float32(2.0 ** -149)
 
+def round_binary32(x):
+    """The binary32 value nearest to the rational x >= 0 (IEEE 754
+    roundTiesToEven: 24-bit significands, subnormals below 2**-126), written
+    from the definition with exact rationals."""
+    x = Fraction(x)
+    if x == 0:
+        return Fraction(0)
+    e = x.numerator.bit_length() - x.denominator.bit_length()
+    if Fraction(2) ** e > x:
+        e -= 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    scaled = x / quantum
+    n = scaled.numerator // scaled.denominator
+    rest = scaled - n
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n * quantum
+
+
+def test_survival_rounds_every_product_to_fp32():
+    """Each survival is the previous one times the next confidence, rounded to
+    binary32 at every step (not the exact product rounded once): checked against
+    exact rationals rounded by the IEEE definition, on chains where the two
+    differ."""
+    rng = np.random.default_rng(77)
+    n, k = 400, 8
+    conf = rng.uniform(0.0, 1.0, (n, k)).astype(np.float32)
+    conf[::7] = (conf[::7] * np.float32(2.0 ** -40)).astype(np.float32)  # into subnormals
+    s, _, _ = oracle.survival(conf, [k] * n, k)
+    differs = 0
+    for r in range(n):
+        chained, exact = Fraction(1), Fraction(1)
+        for j in range(k):
+            c = Fraction(float(conf[r, j]))
+            chained = round_binary32(chained * c)
+            exact *= c
+            assert Fraction(float(s[r, j])) == chained, (r, j)
+            differs += round_binary32(exact) != chained
+    assert differs > 50  # the test tells the two roundings apart
+
+
+def test_ties_go_to_the_lower_request_then_position():
+    """Equal survivals rank by request, then position (the kept sets stay
+    front prefixes either way; the reading fixes which request keeps the slot)."""
+    half = np.full((3, 2), 0.5, dtype=np.float32)  # survivals 0.5, 0.25 everywhere
+    order = oracle.rank_slots(*oracle.survival(half, [2, 2, 2], 2)[:2])
+    assert order == [(0, 0), (1, 0), (2, 0), (0, 1), (1, 1), (2, 1)]
+    assert oracle.budget_allocate(half, [2, 2, 2], 2, 2)["kept"].tolist() == [1, 1, 0]
+    assert oracle.budget_allocate(half, [2, 2, 2], 2, 4)["kept"].tolist() == [2, 1, 1]
+    ones = np.ones((2, 2), dtype=np.float32)  # survival 1 at every slot
+    assert oracle.budget_allocate(ones, [2, 2], 2, 1)["kept"].tolist() == [1, 0]
+    assert oracle.budget_allocate(ones, [2, 2], 2, 3)["kept"].tolist() == [2, 1]
+
+
+def test_fixed_point_is_the_floor():
+    """Budget sums count survivals in whole units of 2**-40, rounding down."""
+    f32 = np.float32
+    assert oracle.fixed_point(f32(1.0)) == 2 ** 40
+    assert oracle.fixed_point(f32(0.5 + 2.0 ** -24)) == 2 ** 39 + 2 ** 16
+    assert oracle.fixed_point(f32(7 * 2.0 ** -42)) == 1   # 1.75 units
+    assert oracle.fixed_point(f32(3 * 2.0 ** -42)) == 0   # 0.75 units
+    assert oracle.fixed_point(f32(2 * 2.0 ** -42)) == 0   # 0.5 units
+    assert oracle.fixed_point(f32(2.0 ** -149)) == 0
+    assert oracle.fixed_point(f32(0.0)) == 0
+
+
 def exhaustive_best(s, lens, cost, t_base, n_bonus):
     """Best allocation over every (b_r) in prod {0..K_r}, exact rationals."""
     n = len(lens)

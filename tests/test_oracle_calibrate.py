@@ -127,11 +127,23 @@ def test_update_moves_toward_the_outcomes():
     assert all_rej[0] < 0 and all_rej[1] == 0  # position 1 never verified
     # x_1 = log2 0.5 = -1 < 0: accepting pushes beta_1 down, rejecting up
     assert all_acc[k] < 0 and all_rej[k] > 0
+    # by hand, at theta = 0 every prediction is 1/2 and x = (-1, 0, 0):
+    # all accepted — 8 verified positions, each with error -1/2, so
+    # grad = (-2, -2, 4, 0, 0) and the step subtracts grad / 8;
+    # all rejected — 4 verified positions (position 0), error +1/2, so
+    # grad = (2, 0, -2, 0, 0) and the step subtracts grad / 4
+    np.testing.assert_array_equal(all_acc, [0.25, 0.25, -0.5, 0.0, 0.0])
+    np.testing.assert_array_equal(all_rej, [-0.5, 0.0, 0.5, 0.0, 0.0])
+    half, _ = cal.calibrate_update(theta, q, [2, 2, 2, 2], cu_from_kept([2] * 4), k, 0.5)
+    np.testing.assert_array_equal(half, all_acc / 2)
 
 
 def test_predict_and_features():
     assert cal.feature(0.0) == -64 and cal.feature(1.0) == 0 and cal.feature(0.25) == -2
     assert cal.feature(float("nan")) == -64 and cal.feature(2.0) == 0
+    # a positive probability below 2**-64 sits at the floor too
+    assert cal.feature(2.0 ** -100) == -64 and cal.feature(2.0 ** -64) == -64
+    assert cal.feature(2.0 ** -63) == -63
     assert cal.entropy_feature(-1.0) == 0 and cal.entropy_feature(float("nan")) == 0
     assert cal.entropy_feature(3.5) == 3.5 and cal.entropy_feature(100.0) == 64
     assert cal.max_feature(-1.0) == 0 and cal.max_feature(float("nan")) == 0

@@ -63,6 +63,23 @@ def test_philox_matches_rocrand(rocrand_ref):
     np.testing.assert_array_equal(got, ref)
 
 
+def test_uniforms_follow_the_rocrand_stream(rocrand_ref):
+    """u and v of (request r, position j, step) are the top 24 bits of words 0
+    and 1 of the block at offset 4 * (r + j * 2**32) of rocRAND's Philox
+    subsequence `step` under the seed, each scaled by 2**-24."""
+    rng = np.random.default_rng(6)
+    cases = [(int(rng.integers(0, 2**63)), int(rng.integers(0, 5000)), int(rng.integers(0, 16)),
+              int(rng.integers(0, 2**40))) for _ in range(500)]
+    cases += [(0, 0, 0, 0), (1, 2, 3, 4), (2**64 - 1, 2**32 - 1, 15, 2**64 - 1)]
+    lines = "".join(f"{s} {st} {4 * (r + (j << 32))}\n" for s, r, j, st in cases)
+    res = subprocess.run([rocrand_ref], input=lines, capture_output=True, text=True, check=True)
+    words = [[int(x) for x in ln.split()] for ln in res.stdout.strip().splitlines()]
+    assert len(words) == len(cases)
+    for (seed, r, j, step), w in zip(cases, words):
+        u, v = oracle.uniforms(seed, r, j, step)
+        assert u == (w[0] >> 8) / 2**24 and v == (w[1] >> 8) / 2**24, (seed, r, j, step)
+
+
 def test_uniforms_are_24_bit_grid_values():
     u, v = oracle.uniforms(123, np.arange(1000), 3, 9)
     for x in (u, v):
