@@ -455,6 +455,20 @@ def timed_plain(torch, iters, fn):
     return time.perf_counter() - t0_
 
 
+def step_percentiles(torch, stream, iters, fn):
+    """p10, median and p90 of one step's time (us): an event at every step
+    boundary of `iters` steps launched back to back on `stream`."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        ev[i].record(stream)
+        fn(i)
+    ev[iters].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]) * 1e3
+    return [round(float(np.percentile(us, q)), 2) for q in (10, 50, 90)]
+
+
 def graph_us(torch, fn, iters):
     """GPU time per call of a small entry point: `iters` calls captured in one
     HIP graph and replayed between two events, so the figure is the kernels'
@@ -605,6 +619,7 @@ def main():
         run_step(i)
     wall = timed_plain(torch, args.steps, run_step)
     wall_eager = timed_plain(torch, args.steps, leg.step) if graphs else wall
+    step_pct = step_percentiles(torch, leg.stream, args.steps, run_step)
     # per-stage times in a separate loop (events between stages cost time)
     for i in range(2):
         leg.step(i)
@@ -782,6 +797,7 @@ def main():
                               if pass2_bytes else None),
         "gpu_step_us": round(float(np.mean(stage_ms.sum(axis=1))) * 1e3, 2),
         "launch": "hip-graph replay" if graphs else "eager",
+        "step_us_p10_p50_p90": step_pct,
         "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 4),
         "step_hbm_gbps": round((pass1_bytes + pass2_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
         "uniform_k": uniform_k,
