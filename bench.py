@@ -51,6 +51,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+SMALL_CALL_ITERS = 1000  # graph-replayed calls per figure for the microsecond entry points
 METRIC = ("verify rows/sec (K+1 rows/req × vocab) + achieved HBM GB/s; "
           "budget-select µs/step")
 
@@ -676,9 +677,10 @@ def main():
     err, bws, cap = leg.err, leg.bws, leg.cap
     uk_k = torch.empty(1, dtype=torch.int32, device=dev)
     uk_kept = torch.empty(n, dtype=torch.int32, device=dev)
+    small_iters = max(SMALL_CALL_ITERS, args.steps)
     uk_us = graph_us(torch, lambda: sv.sv_uniform_k_select(conf_d, dl_d, cost_d, w.t_base,
                                                            w.n_bonus, uk_kept, uk_k, None, err),
-                     args.steps)
+                     small_iters)
     uniform_k = {"us": uk_us, "k": int(uk_k.item()), "drafts_verified": int(uk_kept.sum().item())}
 
     # the step's budget and pack call on its own, graph-replayed: its kernels'
@@ -692,7 +694,17 @@ def main():
         lambda: sv.sv_budget_select_pack(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, last_d,
                                          toks_d, bs_kept, bs_budget, bs_cu, *bs_maps, None, err,
                                          ws=bws),
-        args.steps)
+        small_iters)
+    # and the two calls it fuses, each on its own
+    budget_only_graph_us = graph_us(
+        torch,
+        lambda: sv.sv_budget_select(conf_d, dl_d, cost_d, w.t_base, w.n_bonus, bs_kept,
+                                    bs_budget, None, err, ws=bws),
+        small_iters)
+    pack_graph_us = graph_us(
+        torch,
+        lambda: sv.sv_pack_varlen(bs_kept, last_d, toks_d, bs_cu, *bs_maps, err),
+        small_iters)
 
     # ----------------------------------------- stale-confidence budget leg
     # the pipeline that sizes B one step ahead: the step itself only allocates
@@ -701,7 +713,7 @@ def main():
     budget_allocate_us = graph_us(
         torch, lambda: sv.sv_budget_allocate(conf_d, dl_d, leg.budget, al_kept, None, None, err,
                                              ws=bws),
-        args.steps)
+        small_iters)
 
     # ------------------------------------------ acceptance statistics and calibration leg
     # one verify with the draft-row features, then the per-position counters and
@@ -727,7 +739,7 @@ def main():
             "calibrate_predict_us": lambda: sv.sv_calibrate_predict(
                 theta, leg.q_out, pred, q_entropy=qh, q_max=qm),
         }
-        calibration = {key: graph_us(torch, fn, args.steps) for key, fn in legs.items()}
+        calibration = {key: graph_us(torch, fn, small_iters) for key, fn in legs.items()}
 
     # ---------------------------------- greedy mode on the same workload
     # (same logit replicas and budget; the drafter's argmax ids; pass 1 reads
@@ -788,6 +800,9 @@ def main():
         "budget_pack": "separate" if args.separate_pack else "fused",
         "budget_select_us": round(float(np.mean(stage_ms[:, 0])) * 1e3, 2),
         "budget_select_graph_us": budget_select_graph_us,
+        "budget_select_only_graph_us": budget_only_graph_us,
+        "pack_varlen_graph_us": pack_graph_us,
+        "small_call_iters": small_iters,
         "budget_allocate_us": budget_allocate_us,
         "pack_us": round(float(np.mean(stage_ms[:, 1])) * 1e3, 2),
         "verify_pass1_us": round(pass1_ms * 1e3, 2),
