@@ -449,6 +449,41 @@ def bf16_round(a):
     return torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
 
 
+@pytest.mark.parametrize("dtype,V,ld_pad,tau", [
+    (torch.bfloat16, 129280, 0, 1.0),
+    (torch.bfloat16, 131072, 0, 0.5),   # the largest one-part row
+    (torch.bfloat16, 8193, 0, 1.8),     # a ragged scalar tail
+    (torch.bfloat16, 4100, 0, 1.0),     # a few bonus super-groups
+    (torch.float32, 100003, 0, 0.7),
+    (torch.float32, 65536, 2, 1.0),     # rows off 16-byte alignment
+    (torch.float32, 131073, 0, 1.0),    # two row parts
+])
+def test_verify_bonus_draws(dtype, V, ld_pad, tau):
+    """Every draft accepted (each draft row equals its target row, so p/q = 1):
+    every request's token is a bonus draw from target row b (FOS "평균 수락 길이":
+    the token the target picks itself after the last accepted draft)."""
+    rng = np.random.default_rng(V + ld_pad)
+    n, k = 96, 3
+    kept = rng.integers(0, k + 1, n)
+    cu = np.concatenate([[0], np.cumsum(kept + 1)]).astype(np.int32)
+    target = (rng.standard_normal((int(cu[-1]), V)) * 3).astype(np.float32)
+    if dtype == torch.bfloat16:
+        target = bf16_round(target)
+    draft = np.full((n * k, V), np.nan, dtype=np.float32)
+    toks = np.full((n, k), -1, dtype=np.int32)
+    for r in range(n):
+        for j in range(int(kept[r])):
+            row = target[cu[r] + j]
+            draft[r * k + j] = row
+            toks[r, j] = int(np.argmax(row / tau - np.log(rng.standard_exponential(V))))
+    log(f"bonus draws: {dtype} V={V} ld_pad={ld_pad} tau={tau}")
+    g = gpu_verify(target, draft, toks, cu, k, "stochastic", tau, dtype, seed=V, step=3,
+                   target_ld=V + ld_pad, draft_ld=V + ld_pad)
+    np.testing.assert_array_equal(g["accepted"], kept)
+    stats = compare_verify(g, target, draft, toks, cu, k, V, "stochastic", tau, seed=V, step=3)
+    log(f"  {stats}")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("V,ld_pad", [(1003, 0), (20001, 0), (32, 3), (8192 * 3 + 5, 1),
                                       (1, 0), (7, 0), (131073, 1), (400003, 0)])
