@@ -23,8 +23,10 @@
 // exp2(z * log2(e)/T - offset) in independent
 // fp32 partial sums, so the hot loop has no per-element max; per-thread
 // (offset, sum) pairs merge by rescaling in a fixed tree.  If that shortcut
-// overflows (a later logit more than ~88/T above the first chunk's max) the
-// row is redone exactly (max pass, then sum pass).  Greedy rows track the
+// overflows (a later logit more than ~88/T above the first chunk's max), or a
+// thread whose first chunk held no finite logit meets a part whose whole mass
+// lies below 2^-64 (its own terms may have flushed), the part is redone
+// exactly (max pass, then sum pass).  Greedy rows track the
 // running max and the lowest index reaching it.  Faults: NaN, +inf, or no
 // finite mass.
 //
