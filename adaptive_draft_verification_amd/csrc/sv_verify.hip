@@ -289,11 +289,15 @@ __device__ void row_stats_exact(const char* row, int vocab, float c, float* red,
 // One-pass row statistics; returns through out_a/out_s (identical in every
 // thread).  FEAT also accumulates the entropy term and the largest logit (two
 // more VALU operations per element) into *feat; (a, s) come out bit for bit
-// as without it.
+// as without it.  dtok (or null): where the position's draft id is; thread 0
+// reads it before the stream's first load and, once the first chunk is in
+// (the id with it), the id's logit if the id lies in this part (ids id0 ..
+// id0 + vocab - 1), into *zd: no wave waits for the id before it streams.
 template <sv_dtype DT, bool FEAT = false>
 __device__ void row_stats_stochastic(const char* row, int vocab, float c, float* red,
                                      int* redflag, float* out_a, float* out_s,
-                                     FeatAcc* feat = nullptr) {
+                                     FeatAcc* feat = nullptr, const int32_t* dtok = nullptr,
+                                     float* zd = nullptr, int id0 = 0) {
     using V = Vec<DT>;
     using raw_t = typename V::raw_t;
     constexpr int E = V::kElems;
@@ -325,6 +329,8 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
             mx = fmaxf(mx, x);
         }
     };
+    int did = -1;
+    if (tid == 0 && dtok != nullptr) did = *dtok;
     int i = tid;
     if (i < nvec) {
         float x[E];
@@ -345,6 +351,7 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
             a_t = dflt ? 0.0f : m * c;
         }
     }
+    if (tid == 0 && did >= id0 && did - id0 < vocab) *zd = V::load1(row, did - id0);
     // loads in flight per thread (the feature sums need registers of their own)
     constexpr int U = FEAT ? kFeatUnroll : kUnroll;
     for (; i + (U - 1) * kThreads < nvec; i += U * kThreads) {
@@ -1329,17 +1336,18 @@ __global__ __launch_bounds__(pass1_threads<GREEDY>()) void rowstats_kernel(Args 
         }
         return;
     }
-    // the draft id's logit is fetched up front so its latency hides under the stream
-    const int d = j < b ? a.draft_tokens[(int64_t)r * a.k_max + j] : -1;
-    const bool want_zd = d >= p0 && d < p1;
-    float zd = 0.0f;
-    if (threadIdx.x == 0 && want_zd) zd = Vec<DT>::load1(row, d);
+    // the draft id's logit: fetched by thread 0 inside the stream (ids are
+    // checked in pass 2; one outside [0, vocab) is never in a part)
+    const int32_t* dtok = j < b ? a.draft_tokens + (int64_t)r * a.k_max + j : nullptr;
+    float zd = 0.0f;  // in thread 0, and only if the id lies in [p0, p1)
     float A, S;
     FeatAcc fa;
     if (FEAT && is_draft)
-        row_stats_stochastic<DT, true>(prow, p1 - p0, a.c, redf, redi, &A, &S, &fa);
+        row_stats_stochastic<DT, true>(prow, p1 - p0, a.c, redf, redi, &A, &S, &fa, dtok, &zd,
+                                       p0);
     else
-        row_stats_stochastic<DT>(prow, p1 - p0, a.c, redf, redi, &A, &S);
+        row_stats_stochastic<DT>(prow, p1 - p0, a.c, redf, redi, &A, &S, nullptr, dtok, &zd,
+                                 p0);
     if (FEAT && is_draft && threadIdx.x == 0) {
         FeatPart f;
         f.e = fa.e;
