@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_VALUE, SV_ERR_WORKSPACE, SV_ERR_LAUNCH, \
-    SV_ERR_CAPACITY = range(8)
+    SV_ERR_CAPACITY, SV_ERR_DATA = range(9)
 SV_F32, SV_BF16 = 0, 1
 SV_STOCHASTIC, SV_GREEDY = 0, 1
 SV_DEV_BAD_CU_ROWS, SV_DEV_BAD_TOKEN, SV_DEV_NONFINITE = 1, 2, 4

@@ -73,6 +73,10 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // sv_verify's host checks of everything but the workspace (sv_api.cpp): SV_OK means
 // a launch may follow (nothing to launch when n_req = 0).
 sv_status check_verify(const VerifyArgs& a);
+// The status of a call's launches (sv_api.cpp): SV_ERR_LAUNCH if the runtime
+// refused one; with SV_FORCE_SYNC set (and the stream not capturing) the call
+// also waits for the stream and reports a failed kernel the same way.
+sv_status finish_launch(hipError_t e, hipStream_t stream);
 
 hipError_t launch_accept_stats(const int32_t* accepted, const int32_t* cu_rows, int n_req,
                                int k_max, uint64_t* attempted, uint64_t* accepted_at,

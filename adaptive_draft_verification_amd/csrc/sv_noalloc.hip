@@ -75,5 +75,5 @@ extern "C" sv_status sv_verify_noalloc(const void* target_logits, int64_t target
     const hipError_t e = s != nullptr ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
     if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_LAUNCH;
     if (scratch_address(dev, &a.ws) != hipSuccess) return SV_ERR_LAUNCH;
-    return sv::launch_verify(a, s) == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+    return sv::finish_launch(sv::launch_verify(a, s), s);
 }

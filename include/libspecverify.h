@@ -29,6 +29,19 @@
  *  - Layouts are row-major; int32 token ids; "-1" marks an empty slot, as the
  *    -1 placeholders of the DSD page (section "비동기 스케줄링(Async
  *    Scheduling)과의 호환").
+ *  - Two environment variables, read at every call, serve debugging only (the
+ *    FOS crash write-up: a device fault surfaces at the next synchronisation,
+ *    not where it happened).  SV_FORCE_SYNC=1: after its launches a call
+ *    waits for its stream (not while the stream is being captured into a
+ *    graph) and returns SV_ERR_LAUNCH if one of its kernels failed, so the
+ *    failing call is the one that reports it.  SV_DEBUG_CHECKS=1: before
+ *    launching, sv_verify and sv_verify_stages, the budget calls and
+ *    sv_pack_varlen copy their index inputs (row offsets, draft ids, draft
+ *    lengths, kept counts) to the host, wait for them (not while capturing)
+ *    and return SV_ERR_DATA, launching nothing, where the kernels would set a
+ *    dev_error bit for them.  Both make calls synchronous and slow; neither
+ *    changes any result.  sv_verify_noalloc honours SV_FORCE_SYNC only (its
+ *    contract is to allocate nothing, host memory included).
  */
 #ifndef LIBSPECVERIFY_H
 #define LIBSPECVERIFY_H
@@ -47,8 +60,11 @@ typedef enum {
     SV_ERR_DTYPE = 3,     /* unknown sv_dtype                                  */
     SV_ERR_VALUE = 4,     /* a scalar is out of range (temperature, mode, ...) */
     SV_ERR_WORKSPACE = 5, /* workspace missing or smaller than required        */
-    SV_ERR_LAUNCH = 6,    /* the HIP runtime refused a kernel launch           */
-    SV_ERR_CAPACITY = 7   /* the batch needs more than a static workspace holds */
+    SV_ERR_LAUNCH = 6,    /* the HIP runtime refused a kernel launch, or one failed
+                             (SV_FORCE_SYNC)                                   */
+    SV_ERR_CAPACITY = 7,  /* the batch needs more than a static workspace holds */
+    SV_ERR_DATA = 8       /* index data on the device is inconsistent
+                             (SV_DEBUG_CHECKS only)                            */
 } sv_status;
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;

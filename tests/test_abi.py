@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert sv.sv_status_str(s)
     assert sv.sv_status_str(99) == "unknown status"
 
@@ -300,6 +300,12 @@ def test_binding_constants_match_the_header():
     for name, value in defines.items():
         if hasattr(sv, name):
             assert getattr(sv, name) == int(value), name
+    # the enums: every named value, and the binding has each of them
+    blocks = re.findall(r"typedef enum\s*\{(.*?)\}", text, re.S)
+    enums = dict(re.findall(r"\b(SV_\w+)\s*=\s*(\d+)", " ".join(blocks)))
+    assert enums["SV_ERR_DATA"] == "8" and enums["SV_BF16"] == "1"
+    for name, value in enums.items():
+        assert getattr(sv, name) == int(value), name
 
 
 def test_verify_noalloc_host_validation():

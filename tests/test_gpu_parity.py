@@ -807,6 +807,96 @@ def test_verify_is_deterministic_and_stream_safe():
     assert not np.array_equal(a["tokens"], c["tokens"])
 
 
+def test_debug_environment_variables(monkeypatch):
+    """SV_DEBUG_CHECKS=1 refuses, on the host and before any launch, index data
+    the kernels would flag in dev_error (SV_ERR_DATA; no output touched), and
+    leaves good calls' results as they are; SV_FORCE_SYNC=1 changes no result.
+    Under graph capture both are skipped, and the recorded call replays."""
+    import adaptive_draft_verification_amd as sv
+    rng = np.random.default_rng(77)
+    n, k, V = 12, 3, 4099
+    kept = np.array([3, 0, 2, 1, 3, 3, 0, 1, 2, 3, 1, 2])
+    target, draft, toks, cu = synthetic(rng, n, k, V, kept=kept)
+    t, d = to_dev(target), to_dev(draft)
+    toks_d, cu_d = to_dev(np.asarray(toks, np.int32)), to_dev(np.asarray(cu, np.int32))
+    ref = sv.verify(t, d, toks_d, cu_d, sv.SV_STOCHASTIC, 0.8, 5, 9)
+    monkeypatch.setenv("SV_DEBUG_CHECKS", "1")
+    monkeypatch.setenv("SV_FORCE_SYNC", "1")
+    got = sv.verify(t, d, toks_d, cu_d, sv.SV_STOCHASTIC, 0.8, 5, 9)
+    torch.cuda.synchronize()
+    for key in ref:
+        np.testing.assert_array_equal(ref[key].cpu().numpy(), got[key].cpu().numpy(), key)
+
+    def refused(fn):
+        with pytest.raises(sv.SvError) as e:
+            fn()
+        assert e.value.status == sv.SV_ERR_DATA, e.value
+
+    outs = {key: torch.full_like(v, -5) for key, v in ref.items()}
+    ws = torch.zeros(sv.sv_verify_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+
+    def call(cu_x, toks_x):
+        sv.sv_verify(t, d, toks_x, cu_x, sv.SV_STOCHASTIC, 0.8, 5, 9, outs["tokens"],
+                     outs["accepted"], ws, outs["p_draft"], outs["q_draft"],
+                     outs["residual_mass"], outs["dev_error"])
+
+    bad_cu = np.asarray(cu, np.int32).copy()
+    bad_cu[4] = bad_cu[3] - 1                       # request 3: negative row count
+    refused(lambda: call(to_dev(bad_cu), toks_d))
+    long_cu = np.asarray(cu, np.int32).copy()
+    long_cu[1:] += 1                                 # request 0: k + 1 drafts
+    refused(lambda: call(to_dev(long_cu), toks_d))
+    bad_toks = np.asarray(toks, np.int32).copy()
+    bad_toks[4, 2] = V                               # a kept draft id past the vocabulary
+    refused(lambda: call(cu_d, to_dev(bad_toks)))
+    unkept = np.asarray(toks, np.int32).copy()
+    unkept[1, 0] = -9                                # request 1 keeps nothing: not looked at
+    call(cu_d, to_dev(unkept))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(outs["tokens"].cpu().numpy(), ref["tokens"].cpu().numpy())
+    for key, v in outs.items():
+        v.fill_(-5)
+    refused(lambda: call(to_dev(bad_cu), toks_d))
+    torch.cuda.synchronize()
+    assert (outs["tokens"] == -5).all() and (outs["accepted"] == -5).all()
+
+    # the budget's draft lengths and the pack's kept counts
+    conf = to_dev(rng.uniform(0.1, 1.0, (n, k)).astype(np.float32))
+    cost = to_dev(np.linspace(1.0, 2.0, n * k + 1 + n).astype(np.float32))
+    kept_o = torch.empty(n, dtype=torch.int32, device="cuda")
+    budget = torch.empty(1, dtype=torch.int32, device="cuda")
+    bws = torch.zeros(sv.sv_budget_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    dl = np.full(n, k, np.int32)
+    sv.sv_budget_select(conf, to_dev(dl), cost, n, n, kept_o, budget, ws=bws)
+    dl_bad = dl.copy()
+    dl_bad[7] = k + 1
+    refused(lambda: sv.sv_budget_select(conf, to_dev(dl_bad), cost, n, n, kept_o, budget,
+                                        ws=bws))
+    cap = n * (k + 1)
+    maps = [torch.empty(cap, dtype=torch.int32, device="cuda") for _ in range(3)]
+    cu_o = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+    last = to_dev(np.arange(n, dtype=np.int32))
+    sv.sv_pack_varlen(to_dev(kept.astype(np.int32)), last, toks_d, cu_o, *maps)
+    kept_bad = kept.astype(np.int32).copy()
+    kept_bad[2] = -1
+    refused(lambda: sv.sv_pack_varlen(to_dev(kept_bad), last, toks_d, cu_o, *maps))
+
+    # recorded under capture (the checks and the wait are skipped), then replayed
+    for key, v in outs.items():
+        v.fill_(-5)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        call(cu_d, toks_d)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(outs["tokens"].cpu().numpy(), ref["tokens"].cpu().numpy())
+
+
 def test_end_to_end_path_on_device():
     """budget -> pack -> verify, each stage reading the previous stage's device output."""
     import adaptive_draft_verification_amd as sv
