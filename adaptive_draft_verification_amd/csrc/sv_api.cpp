@@ -127,6 +127,7 @@ const char* sv_status_str(sv_status s) {
         case SV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch, or one failed";
         case SV_ERR_CAPACITY: return "the batch needs more than the static workspace holds";
         case SV_ERR_DATA: return "index data on the device is inconsistent (SV_DEBUG_CHECKS)";
+        default: break;  // the range markers and any other int
     }
     return "unknown status";
 }

@@ -63,12 +63,27 @@ typedef enum {
     SV_ERR_LAUNCH = 6,    /* the HIP runtime refused a kernel launch, or one failed
                              (SV_FORCE_SYNC)                                   */
     SV_ERR_CAPACITY = 7,  /* the batch needs more than a static workspace holds */
-    SV_ERR_DATA = 8       /* index data on the device is inconsistent
+    SV_ERR_DATA = 8,      /* index data on the device is inconsistent
                              (SV_DEBUG_CHECKS only)                            */
+    SV_STATUS_RANGE_LO_ = -2147483647 - 1, /* range markers, never returned: every */
+    SV_STATUS_RANGE_HI_ = 2147483647       /* int32 is a value of the type         */
 } sv_status;
 
-typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
-typedef enum { SV_STOCHASTIC = 0, SV_GREEDY = 1 } sv_mode;
+/* The range markers make every int32 a value of the type (C++ gives an enum
+ * only the range of its enumerators), so that the library can refuse an
+ * unknown dtype or mode that a caller passes as a plain int. */
+typedef enum {
+    SV_F32 = 0,
+    SV_BF16 = 1,
+    SV_DTYPE_RANGE_LO_ = -2147483647 - 1,
+    SV_DTYPE_RANGE_HI_ = 2147483647
+} sv_dtype;
+typedef enum {
+    SV_STOCHASTIC = 0,
+    SV_GREEDY = 1,
+    SV_MODE_RANGE_LO_ = -2147483647 - 1,
+    SV_MODE_RANGE_HI_ = 2147483647
+} sv_mode;
 
 /* Device error bits (ORed into *dev_error). */
 #define SV_DEV_BAD_CU_ROWS   1  /* a request's row range is inconsistent or exceeds target_rows */

@@ -305,7 +305,8 @@ def test_binding_constants_match_the_header():
     enums = dict(re.findall(r"\b(SV_\w+)\s*=\s*(\d+)", " ".join(blocks)))
     assert enums["SV_ERR_DATA"] == "8" and enums["SV_BF16"] == "1"
     for name, value in enums.items():
-        assert getattr(sv, name) == int(value), name
+        if not name.endswith("_"):  # range markers (every int32 a value of the type)
+            assert getattr(sv, name) == int(value), name
 
 
 def test_verify_noalloc_host_validation():
