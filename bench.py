@@ -629,6 +629,7 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     pass1_ms, pass2_ms = float(np.mean(stage_ms[:, 2])), float(np.mean(stage_ms[:, 3]))
+    verify_us = (stage_ms[:, 2] + stage_ms[:, 3]) * 1e3
     roof_ms = leg.pass1_launch_ms(args.steps)
     pass1_bytes = leg.pass1_bytes(rows_t, rows_d)
     pass2_bytes = float(np.mean(p2_rows)) * V * esize
@@ -810,6 +811,12 @@ def main():
         "verify_pass2_bytes": int(pass2_bytes),
         "verify_pass2_frac": (round(pass2_bytes / (pass2_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
                               if pass2_bytes else None),
+        # the verify step alone (both passes, from the staged loop's events)
+        "verify_us_p10_p50_p90": [round(float(np.percentile(verify_us, q)), 2)
+                                  for q in (10, 50, 90)],
+        "verify_rows_per_s": round(rows_t / (float(np.median(verify_us)) * 1e-6), 1),
+        "verify_gbps": round((pass1_bytes + pass2_bytes)
+                             / (float(np.median(verify_us)) * 1e-6) / 1e9, 1),
         "gpu_step_us": round(float(np.mean(stage_ms.sum(axis=1))) * 1e3, 2),
         "launch": "hip-graph replay" if graphs else "eager",
         "step_us_p10_p50_p90": step_pct,
