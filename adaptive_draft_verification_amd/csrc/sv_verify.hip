@@ -18,15 +18,14 @@
 //
 // Row statistics.  The row is streamed once with 16-byte non-temporal loads
 // (each byte is read once; keeping it out of the caches measurably raises
-// the streaming rate).  Stochastic rows keep, per thread, an offset taken
-// from the max of the thread's first 16-byte chunk and accumulate
-// exp2(z * log2(e)/T - offset) in independent
-// fp32 partial sums, so the hot loop has no per-element max; per-thread
-// (offset, sum) pairs merge by rescaling in a fixed tree.  If that shortcut
-// overflows (a later logit more than ~88/T above the first chunk's max), or a
-// thread whose first chunk held no finite logit meets a part whose whole mass
-// lies below 2^-64 (its own terms may have flushed), the part is redone
-// exactly (max pass, then sum pass).  Greedy rows track the
+// the streaming rate).  Stochastic rows keep, per thread, an integer offset
+// and accumulate exp2(z * log2(e)/T - offset) in independent fp32 partial
+// sums; the exponents of each 16-byte chunk are checked before use and the
+// offset moves up (rescaling the sums exactly) when one would enter above 8,
+// so the largest terms are computed from small, accurately rounded
+// exponents.  Per-thread (offset, sum) pairs merge by exact power-of-two
+// scalings in a fixed tree.  A part holding a NaN or +inf, or no finite
+// mass, is redone exactly (max pass, then sum pass).  Greedy rows track the
 // running max and the lowest index reaching it.  Faults: NaN, +inf, or no
 // finite mass.
 //
@@ -149,13 +148,11 @@ struct Vec<SV_F32> {
 };
 
 
-// s * 2^d for d <= 0: 2^(d/2) squared, so that v_exp_f32's flush below 2^-126
-// bites only for d < -252 (a sum below 2^128 then adds less than 2^-124, far
-// below any sum that holds a term near 1).  A sum that is large in its own
-// scale keeps its share when its offset lies far below the other's.
+// s * 2^d for an integer d <= 0, exact (v_ldexp_f32): every offset is an
+// integer, so moving a sum between offsets rounds nothing.  d below -256
+// (a pair without mass, below) gives 0.
 __device__ __forceinline__ float scale_exp2(float s, float d) {
-    const float f = fast_exp2(0.5f * d);
-    return (s * f) * f;
+    return ldexpf(s, (int)fmaxf(d, -256.0f));
 }
 
 // Offset of a pair without mass (a thread that met no finite logit): far
@@ -163,13 +160,27 @@ __device__ __forceinline__ float scale_exp2(float s, float d) {
 // leaves the other pair as it was; two such pairs merge to one.
 constexpr float kNoMass = -1.0e30f;
 
+// Highest exponent t = y - a at which a pass-1 term enters before its
+// thread's offset moves up: with |t| < 8 for the largest terms, the rounding
+// of t (half an ulp of t) costs them at most 2^-22 ln 2 of their value.
+#ifndef SV_REOFFSET
+#define SV_REOFFSET 8.0f
+#endif
+#ifndef SV_REOFFSET_HEADROOM
+#define SV_REOFFSET_HEADROOM 7.0f
+#endif
+constexpr float kReoffset = SV_REOFFSET;
+// A moved offset sits this far above the logit that moved it, so that the
+// next move needs a logit kReoffset + kHeadroom higher: measured on 256 x 8
+// rows of 129280 bf16 N(0, 3^2) logits, a window (-8, 8] costs pass 1
+// ~0.6 us against ~2 us for (-1, 4] (moves in most chunks' waves).
+constexpr float kHeadroom = SV_REOFFSET_HEADROOM;
+
 // Merge two (offset, sum) pairs: both sums re-expressed against the larger
-// offset (scale_exp2 spelled out with an explicit fused multiply-add, so that
-// every caller rounds alike).  A NaN sum propagates.
+// offset (exact scalings; the one rounding is the add).  A NaN sum propagates.
 __device__ __forceinline__ void merge_as(float& a, float& s, float a2, float s2) {
     const float m = fmaxf(a, a2);
-    const float f1 = fast_exp2(0.5f * (a - m)), f2 = fast_exp2(0.5f * (a2 - m));
-    s = fmaf(s * f1, f1, (s2 * f2) * f2);
+    s = scale_exp2(s, a - m) + scale_exp2(s2, a2 - m);
     a = m;
 }
 
@@ -179,9 +190,9 @@ __device__ __forceinline__ void merge_as(float& a, float& s, float a2, float s2)
 __device__ __forceinline__ void merge_ase(float& a, float& s, float& e, float a2, float s2,
                                           float e2) {
     const float m = fmaxf(a, a2);
-    const float f1 = fast_exp2(0.5f * (a - m)), f2 = fast_exp2(0.5f * (a2 - m));
-    e = fmaf(fmaf(a - m, s, e) * f1, f1, (fmaf(a2 - m, s2, e2) * f2) * f2);
-    s = fmaf(s * f1, f1, (s2 * f2) * f2);
+    const float d1 = fmaxf(a - m, -256.0f), d2 = fmaxf(a2 - m, -256.0f);
+    e = scale_exp2(fmaf(d1, s, e), d1) + scale_exp2(fmaf(d2, s2, e2), d2);
+    s = scale_exp2(s, d1) + scale_exp2(s2, d2);
     a = m;
 }
 
@@ -218,8 +229,8 @@ struct FeatAcc {
     float mx = -__builtin_inff();
 };
 
-// Exact two-pass statistics (fallback): offset = max * c, then the sum.  A
-// range holding a NaN or +inf returns S = NaN; one whose logits are all -inf
+// Exact two-pass statistics (fallback): offset = ceil(max * c), then the sum.
+// A range holding a NaN or +inf returns S = NaN; one whose logits are all -inf
 // returns (A, S) = (-inf, 0).
 template <sv_dtype DT, bool FEAT = false>
 __device__ void row_stats_exact(const char* row, int vocab, float c, float* red, float* out_a,
@@ -258,7 +269,7 @@ __device__ void row_stats_exact(const char* row, int vocab, float c, float* red,
         *out_s = 0.0f;
         return;
     }
-    const float a = mx * c;
+    const float a = ceilf(mx * c);
     float s = 0.0f, ef = 0.0f;
     for (int e = tid; e < vocab; e += kThreads) {
         const float t = fmaf(V::load1(row, e), c, -a);
@@ -295,7 +306,7 @@ __device__ void row_stats_exact(const char* row, int vocab, float c, float* red,
 // id0 + vocab - 1), into *zd: no wave waits for the id before it streams.
 template <sv_dtype DT, bool FEAT = false>
 __device__ void row_stats_stochastic(const char* row, int vocab, float c, float* red,
-                                     int* redflag, float* out_a, float* out_s,
+                                     float* out_a, float* out_s,
                                      FeatAcc* feat = nullptr, const int32_t* dtok = nullptr,
                                      float* zd = nullptr, int id0 = 0) {
     using V = Vec<DT>;
@@ -314,14 +325,25 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         eacc[k] = 0.0f;
     }
     float mx = -kInf;
-    float a_t = 0.0f;
-    // dflt: the thread's first element(s) held no finite logit, so its offset
-    // defaulted to 0 and its later terms below 2^-126 flushed to 0 (which
-    // matters only when the whole part lies below about 2^-86, see below)
-    bool dflt = false;
-    // one element: its weight into acc, and with FEAT its entropy term and max
-    auto add = [&](float x, int k) {
-        const float t = fmaf(x, c, -a_t);
+    // The thread's offset: an integer, kNoMass until its first finite logit.
+    // Every term enters at t = y - a_t <= kReoffset (a chunk whose largest
+    // logit would enter higher first moves the offset to ceil(y_max) +
+    // kHeadroom), so the thread's largest terms have |t| < 8 and their
+    // exponents round to within 2^-22 however far the row's peak lies above
+    // its first logits; no sum can overflow.
+    float a_t = kNoMass;
+    auto reoffset = [&](float a_new) {
+        const float d = fmaxf(a_t - a_new, -256.0f);  // an integer below 0
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            if (FEAT) eacc[k] = scale_exp2(fmaf(d, acc[k], eacc[k]), d);
+            acc[k] = scale_exp2(acc[k], d);
+        }
+        a_t = a_new;
+    };
+    // one element at exponent t: its weight into acc, and with FEAT its
+    // entropy term and max
+    auto add = [&](float t, float x, int k) {
         const float w = fast_exp2(t);
         acc[k] += w;
         if (FEAT) {
@@ -329,27 +351,42 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
             mx = fmaxf(mx, x);
         }
     };
+    // one 16-byte chunk (E elements): the exponents against the current
+    // offset, checked (their max, no branch taken unless some lane's chunk
+    // enters too high) before any of them is used
+    auto take = [&](const raw_t& raw) {
+        float x[E], t[E];
+        V::unpack(raw, x);
+#pragma unroll
+        for (int k = 0; k < E; ++k) t[k] = fmaf(x[k], c, -a_t);
+        float m = t[0];
+#pragma unroll
+        for (int k = 1; k < E; ++k) m = fmaxf(m, t[k]);
+        if (m > kReoffset) {
+            float y = x[0];
+#pragma unroll
+            for (int k = 1; k < E; ++k) y = fmaxf(y, x[k]);
+            reoffset(ceilf(y * c) + kHeadroom);
+#pragma unroll
+            for (int k = 0; k < E; ++k) t[k] = fmaf(x[k], c, -a_t);
+        }
+#pragma unroll
+        for (int k = 0; k < E; ++k) add(t[k], x[k], k);
+    };
+    auto take1 = [&](float x) {
+        float t = fmaf(x, c, -a_t);
+        if (t > kReoffset) {
+            reoffset(ceilf(x * c) + kHeadroom);
+            t = fmaf(x, c, -a_t);
+        }
+        add(t, x, 0);
+    };
     int did = -1;
     if (tid == 0 && dtok != nullptr) did = *dtok;
     int i = tid;
     if (i < nvec) {
-        float x[E];
-        V::unpack(stream_load(vrow + i), x);
-        float m = x[0];
-#pragma unroll
-        for (int k = 1; k < E; ++k) m = fmaxf(m, x[k]);
-        dflt = m == -kInf;
-        a_t = dflt ? 0.0f : m * c;
-#pragma unroll
-        for (int k = 0; k < E; ++k) add(x[k], k);
+        take(stream_load(vrow + i));
         i += kThreads;
-    } else {
-        const int e = nvec * E + tid;
-        if (e < vocab) {
-            const float m = V::load1(row, e);
-            dflt = m == -kInf;
-            a_t = dflt ? 0.0f : m * c;
-        }
     }
     if (tid == 0 && did >= id0 && did - id0 < vocab) *zd = V::load1(row, did - id0);
     // loads in flight per thread (the feature sums need registers of their own)
@@ -359,20 +396,10 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
 #pragma unroll
         for (int u = 0; u < U; ++u) w[u] = stream_load(vrow + i + u * kThreads);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float x[E];
-            V::unpack(w[u], x);
-#pragma unroll
-            for (int k = 0; k < E; ++k) add(x[k], k);
-        }
+        for (int u = 0; u < U; ++u) take(w[u]);
     }
-    for (; i < nvec; i += kThreads) {
-        float x[E];
-        V::unpack(stream_load(vrow + i), x);
-#pragma unroll
-        for (int k = 0; k < E; ++k) add(x[k], k);
-    }
-    for (int e = nvec * E + tid; e < vocab; e += kThreads) add(V::load1(row, e), 0);
+    for (; i < nvec; i += kThreads) take(stream_load(vrow + i));
+    for (int e = nvec * E + tid; e < vocab; e += kThreads) take1(V::load1(row, e));
 
     float s = 0.0f, ef = 0.0f;
 #pragma unroll
@@ -394,7 +421,6 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         a = w.a;
         s = w.s;
     }
-    const bool wave_dflt = __ballot(dflt) != 0;
     if (lane == 0) {
         red[4 * wave] = a;
         red[4 * wave + 1] = s;
@@ -402,13 +428,10 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
             red[4 * wave + 2] = ef;
             red[4 * wave + 3] = mx;
         }
-        redflag[wave] = wave_dflt;
     }
     __syncthreads();
     float A = red[0], S = red[1], EF = FEAT ? red[2] : 0.0f, MX = FEAT ? red[3] : -kInf;
-    bool any_dflt = redflag[0] != 0;
     for (int w = 1; w < kThreads / kWave; ++w) {
-        any_dflt |= redflag[w] != 0;
         if (FEAT) {
             merge_ase(A, S, EF, red[4 * w], red[4 * w + 1], red[4 * w + 2]);
             MX = fmaxf(MX, red[4 * w + 3]);
@@ -417,25 +440,21 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         }
     }
     __syncthreads();
-    // Exact path (block-uniform): a NaN or +inf, no mass, an overflowed sum,
-    // or a thread whose offset defaulted to 0 while the part's whole mass
-    // 2^A S lies below 2^-64 (its terms below 2^-126 were flushed, and terms
-    // within 2^-40 of that mass may be among them).
+    // Exact path (block-uniform): a NaN or +inf, no mass, or a sum that is
+    // not finite.
     if (!(S > 0.0f) || !is_finite_bits(S) || !is_finite_bits(A) ||
-        (FEAT && !is_finite_bits(EF)) || (any_dflt && A + log2f(S) < -64.0f)) {
+        (FEAT && !is_finite_bits(EF))) {
         row_stats_exact<DT, FEAT>(row, vocab, c, red, &A, &S, feat);
     } else {
-        // A sum far from 1 (offsets well below the part's largest logit, or a
-        // defaulted offset above it) is brought to [1/2, 1) by moving the
-        // offset, so that the second pass's partial sums of 2^(y - A) cannot
-        // overflow and its terms within 2^-40 of the mass stay normal.
-        if (!(S >= 0x1p-64f && S <= 0x1p64f)) {
-            int k;
-            frexpf(S, &k);
-            if (FEAT) EF = ldexpf(fmaf(-(float)k, S, EF), -k);
-            S = ldexpf(S, -k);
-            A += (float)k;
-        }
+        // S brought to [1/2, 1) by moving the offset by a whole number (both
+        // exact): the part's largest terms then sit within a few units of
+        // t = 0 in the second pass and in p(d), whatever headroom the threads
+        // kept, and the second pass's sums of 2^(y - A) cannot overflow.
+        int k;
+        frexpf(S, &k);
+        if (FEAT) EF = ldexpf(fmaf(-(float)k, S, EF), -k);
+        S = ldexpf(S, -k);
+        A += (float)k;
         if (FEAT) {
             feat->e = EF;
             feat->mx = MX;
@@ -1343,10 +1362,10 @@ __global__ __launch_bounds__(pass1_threads<GREEDY>()) void rowstats_kernel(Args 
     float A, S;
     FeatAcc fa;
     if (FEAT && is_draft)
-        row_stats_stochastic<DT, true>(prow, p1 - p0, a.c, redf, redi, &A, &S, &fa, dtok, &zd,
+        row_stats_stochastic<DT, true>(prow, p1 - p0, a.c, redf, &A, &S, &fa, dtok, &zd,
                                        p0);
     else
-        row_stats_stochastic<DT>(prow, p1 - p0, a.c, redf, redi, &A, &S, nullptr, dtok, &zd,
+        row_stats_stochastic<DT>(prow, p1 - p0, a.c, redf, &A, &S, nullptr, dtok, &zd,
                                  p0);
     if (FEAT && is_draft && threadIdx.x == 0) {
         FeatPart f;

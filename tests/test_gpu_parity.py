@@ -502,11 +502,14 @@ def test_verify_ragged_vocab_and_strides(dtype, V, ld_pad, mode):
                    3, 11)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", list(range(16)) + [41, 48, 59, 84, 119, 151, 172, 194, 228])
 def test_verify_random_shapes(seed):
     """Seeded random shapes: batch, draft count, vocabulary (one super-group
     to several row parts' worth of groups), row stride, dtype, mode,
-    temperature, Philox step and kept counts, each against the oracle."""
+    temperature, Philox step and kept counts, each against the oracle.
+    Seeds 41 to 228 draw peaked rows (logit scale 8, or T = 0.3) with small
+    residual masses, which exponents rounded far from the row's peak once
+    put outside the residual-mass tolerance."""
     rng = np.random.default_rng(1000 + seed)
     n = int(rng.integers(1, 25))
     k = int(rng.integers(0, 10))
