@@ -342,44 +342,49 @@ __device__ void row_stats_stochastic(const char* row, int vocab, float c, float*
         a_t = a_new;
     };
     // one element at exponent t: its weight into acc, and with FEAT its
-    // entropy term and max
-    auto add = [&](float t, float x, int k) {
+    // entropy term
+    auto add = [&](float t, int k) {
         const float w = fast_exp2(t);
         acc[k] += w;
-        if (FEAT) {
-            eacc[k] = fmaf(w, fmaxf(t, kTFloor), eacc[k]);
-            mx = fmaxf(mx, x);
-        }
+        if (FEAT) eacc[k] = fmaf(w, fmaxf(t, kTFloor), eacc[k]);
     };
-    // one 16-byte chunk (E elements): the exponents against the current
-    // offset, checked (their max, no branch taken unless some lane's chunk
-    // enters too high) before any of them is used
+    // one 16-byte chunk (E elements), checked before any exponent is used
+    // (no branch taken unless some lane's chunk enters too high): plain rows
+    // check the max of the exponents against the current offset; with FEAT
+    // the chunk's largest logit, which the features keep anyway
     auto take = [&](const raw_t& raw) {
         float x[E], t[E];
         V::unpack(raw, x);
-#pragma unroll
-        for (int k = 0; k < E; ++k) t[k] = fmaf(x[k], c, -a_t);
-        float m = t[0];
-#pragma unroll
-        for (int k = 1; k < E; ++k) m = fmaxf(m, t[k]);
-        if (m > kReoffset) {
+        if (FEAT) {
             float y = x[0];
 #pragma unroll
             for (int k = 1; k < E; ++k) y = fmaxf(y, x[k]);
-            reoffset(ceilf(y * c) + kHeadroom);
+            mx = fmaxf(mx, y);
+            if (fmaf(y, c, -a_t) > kReoffset) reoffset(ceilf(y * c) + kHeadroom);
 #pragma unroll
             for (int k = 0; k < E; ++k) t[k] = fmaf(x[k], c, -a_t);
+        } else {
+#pragma unroll
+            for (int k = 0; k < E; ++k) t[k] = fmaf(x[k], c, -a_t);
+            float m = t[0];
+#pragma unroll
+            for (int k = 1; k < E; ++k) m = fmaxf(m, t[k]);
+            if (m > kReoffset) {
+                float y = x[0];
+#pragma unroll
+                for (int k = 1; k < E; ++k) y = fmaxf(y, x[k]);
+                reoffset(ceilf(y * c) + kHeadroom);
+#pragma unroll
+                for (int k = 0; k < E; ++k) t[k] = fmaf(x[k], c, -a_t);
+            }
         }
 #pragma unroll
-        for (int k = 0; k < E; ++k) add(t[k], x[k], k);
+        for (int k = 0; k < E; ++k) add(t[k], k);
     };
     auto take1 = [&](float x) {
-        float t = fmaf(x, c, -a_t);
-        if (t > kReoffset) {
-            reoffset(ceilf(x * c) + kHeadroom);
-            t = fmaf(x, c, -a_t);
-        }
-        add(t, x, 0);
+        if (FEAT) mx = fmaxf(mx, x);
+        if (fmaf(x, c, -a_t) > kReoffset) reoffset(ceilf(x * c) + kHeadroom);
+        add(fmaf(x, c, -a_t), 0);
     };
     int did = -1;
     if (tid == 0 && dtok != nullptr) did = *dtok;
