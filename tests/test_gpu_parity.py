@@ -664,6 +664,53 @@ def test_verify_low_temperature_and_ties():
     compare_verify(g, target, None, toks, cu, k, V, "greedy", 1.0)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("tau", [0.5, 1.0])
+def test_verify_rising_and_outlier_rows(dtype, tau):
+    """Rows that move pass 1's per-thread offsets again and again: a steep
+    ramp (every chunk of every thread enters far above the offset before it),
+    ascending and descending sorted rows, and a single outlier far above the
+    rest at the last id or at id 0 (the id holds nearly all of p).  The
+    entropy and largest-probability features ride along, so their rescaling
+    on each move is checked too."""
+    rng = np.random.default_rng(97)
+    n, k, V = 6, 3, 20001
+    kept = np.full(n, k)
+    cu = np.concatenate([[0], np.cumsum(kept + 1)]).astype(np.int32)
+    rows = int(cu[-1])
+    target = (rng.standard_normal((rows, V)) * 3).astype(np.float32)
+    ids = np.arange(V, dtype=np.float32)
+    for r in range(n):
+        for j in range(k + 1):
+            t = target[cu[r] + j]
+            if r == 0:
+                t[:] = ids * 0.01 - 100.0            # ramp from -100 to +100
+            elif r == 1:
+                t[:] = np.sort(t)                    # ascending
+            elif r == 2:
+                t[:] = np.sort(t)[::-1]              # descending
+            elif r == 3:
+                t[-1] = 60.0                         # outlier at the last id
+            elif r == 4:
+                t[0] = 60.0                          # outlier at id 0
+            else:
+                t[:] = -ids * 0.01 + 50.0            # falling ramp
+    draft = np.full((n * k, V), np.nan, dtype=np.float32)
+    toks = np.full((n, k), -1, dtype=np.int32)
+    for r in range(n):
+        for j in range(k):
+            row = target[cu[r] + j] + rng.standard_normal(V).astype(np.float32)
+            draft[r * k + j] = row
+            toks[r, j] = int(np.argmax(row / tau - np.log(rng.standard_exponential(V))))
+    if dtype == torch.bfloat16:
+        target, draft = bf16_round(target), bf16_round(draft)
+    log(f"rising and outlier rows: {dtype} tau={tau}")
+    for step in range(3):
+        g = gpu_verify(target, draft, toks, cu, k, "stochastic", tau, dtype, seed=4, step=step,
+                       features=True)
+        compare_verify(g, target, draft, toks, cu, k, V, "stochastic", tau, 4, step)
+
+
 def test_verify_draw_lands_on_positive_weight():
     """Residuals with zero weight on every other id, drawn many times: every
     drawn id must carry weight (the oracle's rule never lands on a zero)."""
