@@ -37,7 +37,9 @@
 // counter and stream them (the next
 // one's loads in flight while the current one is summed, no barrier in the
 // stream), each super-group's sum goes to LDS, and wave 0 walks the sums in
-// id order and reads only the crossing super-group again.
+// id order and reads only the crossing super-group again.  The bonus row's
+// total is pass 1's sum, so its draw stops claiming once the super-groups
+// already summed pass v * W.
 #include "sv_device.h"
 #include "sv_launch.h"
 
@@ -720,6 +722,7 @@ struct DrawSmem {
     int next;                // next unclaimed super-group
     int tok;                 // the drawn id
     float total;             // W
+    float done;              // known W: the sum of the super-groups finished so far
 };
 
 // Per-thread sum of 8 weights, in id order.
@@ -789,10 +792,15 @@ __device__ __forceinline__ float group_lane_sum(const DrawRow& d, int g, int lan
 // If rounding leaves v * W at or above the running total, the last id of
 // positive weight is taken.  Only ids of positive weight are ever drawn.
 // *mass gets W; returns -2 if W is not positive.
+// w_known > 0 (a draw from one row whose total pass 1 has summed): W is
+// w_known, so v * W is known before the sweep, and the waves stop claiming
+// once the super-groups already finished sum past it with a margin that
+// covers every rounding of both sums (claims go out in id order, so the
+// crossing then lies among the claimed ones); the walk covers those.
 template <sv_dtype DT, bool RESID>
 __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, float ap,
                         float aq, float rq, float v, DrawSmem& sm, float* mass,
-                        bool claims_ready = false) {
+                        bool claims_ready = false, float w_known = 0.0f) {
     using G = Geom<DT, RESID>;
     constexpr int kGroupIds = G::kIds;
     constexpr int kIdsPerLane = G::kIdsPerLane;
@@ -809,10 +817,19 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
     d.rq = rq;
     const int n_groups = (vocab + kGroupIds - 1) / kGroupIds;
 
-    // ---- 1. sweep (claims_ready: sm.next was set before a barrier the
-    // caller has passed)
+    // ---- 1. sweep (claims_ready: sm.next and sm.done were set before a
+    // barrier the caller has passed)
+    const bool early = !RESID && w_known > 0.0f;
+    // the finished super-groups' sum (in any order) and the walk's (in id
+    // order) each lie within n_groups * 2^-24 of their exact sums, n_groups
+    // <= 2^11: a finished sum above v W (1 + 2^-10) puts the walk's
+    // running sum over the claimed super-groups above v W
+    const float stop_at = v * w_known * (1.0f + 0x1p-10f);
     if (!claims_ready) {
-        if (tid == 0) sm.next = kP2Waves;
+        if (tid == 0) {
+            sm.next = kP2Waves;
+            sm.done = 0.0f;
+        }
         __syncthreads();
     }
     {
@@ -821,9 +838,18 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
         // partial super-group, or every one of an unaligned row) element-wise
         const int n_fast = d.aligned ? (d.vocab & ~7) / kGroupIds : 0;
         auto claim = [&]() {
-            int g2 = 0;
-            if (lane == 0) g2 = atomicAdd(&sm.next, 1);
+            int g2 = n_groups;  // no further claim
+            if (lane == 0 &&
+                (!early || __hip_atomic_load(&sm.done, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP) <= stop_at))
+                g2 = atomicAdd(&sm.next, 1);
             return __builtin_amdgcn_readfirstlane(g2);
+        };
+        auto publish = [&](int g, float gs) {
+            if (lane == 0) {
+                sm.gsum[g] = gs;
+                if (early) atomicAdd(&sm.done, gs);
+            }
         };
         int g = wave;  // the first claim of each wave is implicit
         GroupRaw<DT, RESID> ba, bb;
@@ -832,18 +858,18 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
             int g2 = claim();
             if (g2 < n_fast) group_fetch<DT, RESID>(d, g2, lane, bb);
             float gs = wave_sum_dpp(group_lane_sum<DT, RESID>(d, g, lane, true, ba), lane);
-            if (lane == 0) sm.gsum[g] = gs;
+            publish(g, gs);
             g = g2;
             if (g >= n_fast) break;
             g2 = claim();
             if (g2 < n_fast) group_fetch<DT, RESID>(d, g2, lane, ba);
             gs = wave_sum_dpp(group_lane_sum<DT, RESID>(d, g, lane, true, bb), lane);
-            if (lane == 0) sm.gsum[g] = gs;
+            publish(g, gs);
             g = g2;
         }
         while (g < n_groups) {
             const float gs = wave_sum_dpp(group_lane_sum<DT, RESID>(d, g, lane, false, ba), lane);
-            if (lane == 0) sm.gsum[g] = gs;
+            publish(g, gs);
             g = claim();
         }
     }
@@ -851,53 +877,57 @@ __device__ int draw_row(const char* prow, const char* qrow, int vocab, float c, 
 
     // ---- 2. walk and second look (wave 0)
     if (wave == 0) {
-        // lane l owns super-groups [l G, (l + 1) G), G = ceil(n_groups / 64):
-        // every lane a few, however long the row
+        // the super-groups swept: every one below the claim counter (all of
+        // them unless the sweep stopped early)
+        const int n_swept = min(sm.next, n_groups);
+        // lane l owns super-groups [l G, (l + 1) G), G = ceil(n_groups / 64)
+        // (every lane a few, however long the row).  The running sum at a
+        // super-group is its lane's base (an exclusive wave scan of the lane
+        // sums) plus the lane's own super-groups up to it, in order: it
+        // depends only on the super-groups at or before it, so an early stop
+        // past the crossing changes nothing.
         const int gpl = (n_groups + kWave - 1) / kWave;
+        const int g_lo = lane * gpl, g_hi = min(g_lo + gpl, n_swept);
         float lsum = 0.0f;
-        bool lpos = false;
-        for (int i = 0; i < gpl; ++i) {
-            const int g = lane * gpl + i;
-            if (g < n_groups) {
-                lsum += sm.gsum[g];
-                lpos |= sm.gsum[g] > 0.0f;
-            }
+        int lastg = -1;  // the lane's last positive super-group
+        for (int g = g_lo; g < g_hi; ++g) {
+            const float x = sm.gsum[g];
+            lsum += x;
+            if (x > 0.0f) lastg = g;
         }
         const float incl = wave_incl_sum_dpp(lsum, lane);
-        const float W = lane63(incl);
+        // the lane below's inclusive sum (DPP wave_shr:1; lane 0 reads 0)
+        const float excl = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(incl), 0x138, 0xf, 0xf, false));
+        const float swept = lane63(incl);
+        const float W = early ? w_known : swept;
         int tok = -2;
-        if (W > 0.0f) {
+        if (W > 0.0f && swept > 0.0f) {
             const float tgt = v * W;
-            // the walk, in every lane of wave 0: the first lane holding a
-            // positive super-group whose running sum passes tgt, then its first
-            // positive super-group doing so.  W > 0, so some lane holds a
-            // positive super-group; the walk never leaves the positive ones.
-            const uint64_t pos = __ballot(lpos);
-            const uint64_t past = __ballot(lpos && incl > tgt);
-            bool crossing = past != 0;
-            const int hl = crossing ? __builtin_ctzll(past) : 63 - __builtin_clzll(pos);
-            // lane hl's super-groups, one per lane, with a wave scan: the
-            // running sum before and after each
-            // exclusive prefix of lane hl (hl is the same in every lane)
-            const float base = readlane_t(incl - lsum, hl);
-            const int gi = hl * gpl + lane;
-            const float x = (lane < gpl && gi < n_groups) ? sm.gsum[gi] : 0.0f;
-            const float xi = wave_incl_sum_dpp(x, lane);
-            // the lane below's inclusive sum (DPP wave_shr:1; lane 0 reads 0)
-            const float xe = __int_as_float(
-                __builtin_amdgcn_update_dpp(0, __float_as_int(xi), 0x138, 0xf, 0xf, false));
-            const float before = base + xe;
-            const bool posg = x > 0.0f;
-            const uint64_t hitm = __ballot(crossing && posg && base + xi > tgt);
-            int hit_lane;
-            if (hitm) {
-                hit_lane = __builtin_ctzll(hitm);
-            } else {  // rounding: the last positive id of the lane's last positive group
-                crossing = false;
-                hit_lane = 63 - __builtin_clzll(__ballot(posg));
+            // the first positive super-group whose running sum passes tgt
+            float run = excl, fbase = 0.0f;
+            int found = -1;
+            for (int g = g_lo; g < g_hi; ++g) {
+                const float x = sm.gsum[g];
+                const float nr = run + x;
+                if (found < 0 && x > 0.0f && nr > tgt) {
+                    found = g;
+                    fbase = run;
+                }
+                run = nr;
             }
-            const int hit = hl * gpl + hit_lane;
-            const float hit_base = readlane_t(before, hit_lane);
+            const uint64_t fm = __ballot(found >= 0);
+            bool crossing = fm != 0;
+            int hit;
+            float hit_base = 0.0f;
+            if (crossing) {
+                const int hl = __builtin_ctzll(fm);
+                hit = __builtin_amdgcn_readlane(found, hl);
+                hit_base = readlane_t(fbase, hl);
+            } else {  // rounding: the last positive id of the last positive super-group
+                const uint64_t pm = __ballot(lastg >= 0);
+                hit = __builtin_amdgcn_readlane(lastg, 63 - __builtin_clzll(pm));
+            }
             // second look: lane l takes ids [g0 + l n, g0 + (l + 1) n), n = kIdsPerLane
             const int e0 = hit * kGroupIds + lane * kIdsPerLane;
             float wts[kIdsPerLane];
@@ -1162,7 +1192,10 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
             sm.b = b;
             sm.lo = lo;
             sm.fault = fault;
-            if (!GREEDY) sm.draw.next = kP2Waves;  // the draw's first claims are implicit
+            if (!GREEDY) {
+                sm.draw.next = kP2Waves;  // the draw's first claims are implicit
+                sm.draw.done = 0.0f;
+            }
         }
         // Every output the draw does not decide is written now, by the lane of
         // its position: the accepted drafts, the -1 after L, the per-position
@@ -1209,12 +1242,12 @@ __device__ void finish_request(const Args& a, int r, FinishSmem& sm) {
             if (token == -2) {  // zero residual mass: draw from p instead
                 float unused;
                 token = draw_row<DT, false>(prow, prow, a.vocab, a.c, tA, 0.0f, 1.0f, v, sm.draw,
-                                            &unused);
+                                            &unused, false, tS);
             }
         } else {
             float unused;
             token = draw_row<DT, false>(prow, prow, a.vocab, a.c, sm.ba, 0.0f, 1.0f, v, sm.draw,
-                                        &unused, true);
+                                        &unused, true, sm.bs);
         }
     }
     if (token < 0) {  // no id carries weight: only reachable through a numeric fault

@@ -325,18 +325,25 @@ class Leg:
                                 self.q_out, self.res_out, self.err, vocab=w.vocab)
             mark(2 + stage)
 
-    def pass2_rows(self, steps, kept_h_, **kw):
-        """Rows the draws re-read in each of `steps` (deterministic: same step index,
-        same draws): two per rejected request, one per request that accepted all."""
+    def pass2_ids(self, steps, kept_h_, **kw):
+        """Logits the draws must re-read in each of `steps` (deterministic: same step
+        index, same draws): both rows whole for a rejected request (the residual's
+        total needs every id), and for a request that accepted every draft the bonus
+        row's ids up to the drawn one (its total comes from pass 1, so the draw's
+        sweep stops once it has passed the drawn id)."""
         if self.mode == self.sv.SV_GREEDY:
             return np.zeros(len(steps))
         out = []
-        n = self.w.n
+        V = self.w.vocab
+        kept = np.asarray(kept_h_)
         for i in steps:
             self.step(i, **kw)
             acc = self.acc_out.cpu().numpy()
-            rej = int(((acc >= 0) & (acc < kept_h_)).sum())
-            out.append(2 * rej + (n - rej))
+            tok = self.tok_out.cpu().numpy()
+            rej = (acc >= 0) & (acc < kept)
+            bonus = (acc >= 0) & (acc == kept)
+            drawn = tok[np.arange(len(acc)), np.clip(acc, 0, None)]
+            out.append(2 * V * int(rej.sum()) + int((drawn[bonus] + 1).sum()))
         return np.array(out, dtype=np.float64)
 
     def timed(self, iters, **kw):
@@ -414,10 +421,10 @@ class Leg:
         for i in range(2):
             self.step(i)
         _, stage_ms = self.timed(steps)
-        p2_rows = self.pass2_rows(range(steps), self.kept_h)
+        p2_ids = self.pass2_ids(range(steps), self.kept_h)
         p1_ms = self.pass1_launch_ms(steps)
         p1_bytes = self.pass1_bytes(self.rows_t, self.rows_d)
-        p2_bytes = float(np.mean(p2_rows)) * self.w.vocab * self.esize
+        p2_bytes = float(np.mean(p2_ids)) * self.esize
         p2_ms = float(np.mean(stage_ms[:, 3]))
         out = {
             "workload": self.w.name, "mode": self.mode_name, "logits": self.w.dtype,
@@ -625,14 +632,14 @@ def main():
     for i in range(2):
         leg.step(i)
     _, stage_ms = leg.timed(args.steps)
-    p2_rows = leg.pass2_rows(range(args.steps), leg.kept_h)
+    p2_ids = leg.pass2_ids(range(args.steps), leg.kept_h)
 
     ms_per_step = wall * 1e3 / args.steps
     pass1_ms, pass2_ms = float(np.mean(stage_ms[:, 2])), float(np.mean(stage_ms[:, 3]))
     verify_us = (stage_ms[:, 2] + stage_ms[:, 3]) * 1e3
     roof_ms = leg.pass1_launch_ms(args.steps)
     pass1_bytes = leg.pass1_bytes(rows_t, rows_d)
-    pass2_bytes = float(np.mean(p2_rows)) * V * esize
+    pass2_bytes = float(np.mean(p2_ids)) * esize
     achieved = pass1_bytes / (roof_ms * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- full K leg
@@ -645,8 +652,8 @@ def main():
         _, fms = leg.timed(args.full_k_iters, **kw)
         f1, f2 = float(np.mean(fms[:, 2])), float(np.mean(fms[:, 3]))
         f_p1 = leg.pass1_bytes(rows_tf, rows_df)
-        f_p2 = float(np.mean(leg.pass2_rows(range(args.full_k_iters), w.draft_len, **kw))) \
-            * V * esize
+        f_p2 = float(np.mean(leg.pass2_ids(range(args.full_k_iters), w.draft_len, **kw))) \
+            * esize
         f1_launch = leg.pass1_launch_ms(args.full_k_iters, reps=full_reps, cu_rows=cu_full)
         full = {
             "target_rows": rows_tf, "draft_rows": rows_df,
