@@ -213,17 +213,15 @@ __device__ __forceinline__ T waves_before(const T* tot, int wave, int lane, T* a
     return readlane_t(incl - x, wave);
 }
 
-// (score, B) pair; the better one has the larger score, then the smaller B.
+// A wave's best (score, B): the larger score, then the smaller B.
 struct Cand {
     double score;
     int32_t b;
     int32_t pad;
 };
 
-struct BetterOp {
-    __device__ __forceinline__ Cand operator()(Cand a, Cand c) const {
-        return (c.score > a.score || (c.score == a.score && c.b < a.b)) ? c : a;
-    }
+struct MaxOpD {
+    __device__ __forceinline__ double operator()(double a, double b) const { return fmax(a, b); }
 };
 
 // kept[r] = #{j : rank(r, j) < B}.  A request's real slots rank in position
@@ -417,14 +415,18 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
     uint64_t run_sum = incl - local + waves_before(wave_tot, wave, lane, &all_waves);
     (void)all_waves;
 
-    Cand best{-__builtin_inf(), 0x7fffffff, 0};
+    // this thread's best candidate; its B values rise with the thread and the
+    // lane, so the first maximiser of the block is the lowest lane holding the
+    // maximum score (strict > keeps a thread's smaller B on a tie)
+    double bs = -__builtin_inf();
+    int bb = 0x7fffffff;
     int cost_err = 0;
     if (tid == 0) {  // B = 0
         if (cost0 > 0.0f && is_finite_bits(cost0))
-            best.score = (double)n_bonus / (double)cost0;
+            bs = (double)n_bonus / (double)cost0;
         else
             cost_err = SV_DEV_BAD_COST;
-        best.b = 0;
+        bb = 0;
     }
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
@@ -435,19 +437,28 @@ __global__ __launch_bounds__(kThreads) void finish_kernel(
             if (cst[q] > 0.0f && is_finite_bits(cst[q])) {
                 // run_sum < 2^53 and 2^-40 is a power of two: the product is exact
                 const double sc = ((double)n_bonus + (double)run_sum * 0x1p-40) / (double)cst[q];
-                best = BetterOp{}(best, Cand{sc, rank + 1, 0});
+                if (sc > bs) {
+                    bs = sc;
+                    bb = rank + 1;
+                }
             } else {
                 cost_err = SV_DEV_BAD_COST;
             }
         }
     }
-    best = lane63(wave_scan_dpp(best, lane, BetterOp{}));
-    if (cost_err) atomicOr(&err_s, cost_err);
-    if (lane == 0) wave_best[wave] = best;
+    {
+        const double m = lane63(wave_scan_dpp(bs, lane, MaxOpD{}));
+        const int wb = __builtin_amdgcn_readlane(bb, __builtin_ctzll(__ballot(bs == m)));
+        if (cost_err) atomicOr(&err_s, cost_err);
+        if (lane == 0) wave_best[wave] = Cand{m, wb, 0};
+    }
     __syncthreads();
-    // every wave reduces the 16 wave winners itself: no further barrier
-    Cand c = lane < kWaves ? wave_best[lane] : Cand{-__builtin_inf(), 0x7fffffff, 0};
-    const int B = lane63(wave_scan_dpp(c, lane, BetterOp{})).b;
+    // every wave reduces the 16 wave winners itself (waves in B order too): no
+    // further barrier
+    const double cs = lane < kWaves ? wave_best[lane].score : -__builtin_inf();
+    const int cb = lane < kWaves ? wave_best[lane].b : 0x7fffffff;
+    const double cm = lane63(wave_scan_dpp(cs, lane, MaxOpD{}));
+    const int B = __builtin_amdgcn_readlane(cb, __builtin_ctzll(__ballot(cs == cm)));
     write_kept(rk, rk1, per, B, n_req, k_max, kept, PACK ? kept_s : nullptr);
     if (tid == 0) {
         budget[0] = B;
