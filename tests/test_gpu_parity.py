@@ -482,6 +482,14 @@ def test_verify_bonus_draws(dtype, V, ld_pad, tau):
     np.testing.assert_array_equal(g["accepted"], kept)
     stats = compare_verify(g, target, draft, toks, cu, k, V, "stochastic", tau, seed=V, step=3)
     log(f"  {stats}")
+    # A bonus draw stops its sweep once the summed super-groups pass v * W,
+    # which happens at a time that varies from call to call; the drawn ids
+    # must not: repeated calls agree bit for bit.
+    for _ in range(8):
+        again = gpu_verify(target, draft, toks, cu, k, "stochastic", tau, dtype, seed=V, step=3,
+                           target_ld=V + ld_pad, draft_ld=V + ld_pad)
+        for key in ("tokens", "accepted", "p_draft", "q_draft", "residual_mass"):
+            np.testing.assert_array_equal(again[key], g[key], err_msg=key)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
