@@ -716,6 +716,10 @@ struct Geom {
 constexpr int kMaxGroupsAny = Geom<SV_F32, true>::kMaxGroups > Geom<SV_BF16, true>::kMaxGroups
                                   ? Geom<SV_F32, true>::kMaxGroups
                                   : Geom<SV_BF16, true>::kMaxGroups;
+// the early stop of a draw with a known total takes its margin from at most
+// 2^11 super-groups a row
+static_assert(Geom<SV_F32, false>::kMaxGroups <= 2048 && Geom<SV_BF16, false>::kMaxGroups <= 2048,
+              "the early stop's rounding margin assumes at most 2^11 super-groups");
 
 struct DrawSmem {
     float gsum[kMaxGroupsAny];  // per super-group weight sums
