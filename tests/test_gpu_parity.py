@@ -641,8 +641,11 @@ def test_verify_bad_offsets_never_read_past_target_rows():
         assert int(g["dev_error"][0]) & oracle.DEV_BAD_CU_ROWS
 
 
-def test_verify_exact_fallback_for_late_large_logit():
-    """A logit far above the first chunk's maximum forces the exact two-pass path."""
+def test_verify_late_large_logit():
+    """A logit far above the rest of its row, late in the row (the thread that
+    meets it moves its offset by ~260 at once, its earlier sums scaling to
+    nothing), one in a draft row, and a row whose logits drop by 120 after id
+    5 (offsets set early lie far above the rest)."""
     rng = np.random.default_rng(29)
     n, k, V = 4, 2, 70000
     target, draft, toks, cu = synthetic(rng, n, k, V, [2, 2, 2, 2])
@@ -768,8 +771,8 @@ def _far_rows(rng, n, k, V, center, spread, masked, tau):
 def test_verify_far_negative_logits(dtype, V, center, spread, masked, tau):
     """Rows whose whole mass lies near the bottom of fp32's normal range, with and
     without a masked prefix: threads that meet no finite logit first, or no id at
-    all, must not move the row's offset, and terms that a defaulted offset would
-    flush must be recovered (the exact path)."""
+    all, must not move the row's offset, and no term may flush (each thread takes
+    its terms within a few units of its own largest logit)."""
     rng = np.random.default_rng(V + masked)
     n, k = 4, 3
     target, draft, toks, cu = _far_rows(rng, n, k, V, center, spread, masked, tau)
@@ -786,9 +789,10 @@ def test_verify_far_negative_logits(dtype, V, center, spread, masked, tau):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_verify_finite_mask_far_below_the_row(dtype):
     """Ids masked with a finite logit (-88) in every first chunk of half the
-    threads, whose later ids sit 9 below the rest: their sums are large in their
-    own scale and their offsets lie more than 126 (log2 units) below the row's,
-    so a rescale that flushed below 2^-126 would drop ~1e-4 of the mass."""
+    threads, whose later ids sit 9 below the rest: those threads first take an
+    offset more than 126 (log2 units) below the row's and then move it, and their
+    sums, large in their own scale, must survive the moves and the merges (a
+    rescale that flushed below 2^-126 would drop ~1e-4 of the mass)."""
     E = 8 if dtype == torch.bfloat16 else 4
     rng = np.random.default_rng(61)
     n, k, V = 3, 2, 6144
