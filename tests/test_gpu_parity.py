@@ -539,6 +539,37 @@ def test_verify_random_shapes(seed):
     compare_verify(g, target, dmode, toks, cu, k, V, mode, tau, seed, step)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_verify_random_large_vocab(seed):
+    """Seeded random batches at vocabularies of 100,000 to SV_MAX_VOCAB ids
+    (two to eight row parts whose offsets and sums merge in pass 2), both
+    dtypes, peaked and flat rows; every other case accepts every draft, so
+    its tokens are bonus draws whose sweeps stop early."""
+    import adaptive_draft_verification_amd as sv
+    rng = np.random.default_rng(60000 + seed)
+    n = int(rng.integers(1, 6))
+    k = int(rng.integers(1, 8))
+    V = int(rng.choice([int(rng.integers(100000, 300000)),
+                        int(rng.integers(300000, sv.SV_MAX_VOCAB + 1))]))
+    dtype = torch.bfloat16 if seed % 2 == 0 else torch.float32
+    mode = "greedy" if seed == 7 else "stochastic"
+    tau = float(rng.choice([0.3, 0.7, 1.0, 1.8]))
+    step = int(rng.integers(0, 2 ** 40))
+    ld_pad = int(rng.integers(0, 3))
+    target, draft, toks, cu = synthetic(rng, n, k, V, scale=float(rng.choice([1.0, 3.0, 8.0])))
+    if seed % 2 == 1:
+        for r in range(n):
+            for j in range(int(cu[r + 1] - cu[r] - 1)):
+                draft[r * k + j] = target[cu[r] + j]
+    if dtype == torch.bfloat16:
+        target, draft = bf16_round(target), bf16_round(draft)
+    log(f"large vocab seed={seed}: n={n} k={k} V={V} {dtype} {mode} tau={tau}")
+    dmode = draft if mode == "stochastic" else None
+    g = gpu_verify(target, dmode, toks, cu, k, mode, tau, dtype, seed=seed, step=step,
+                   target_ld=V + ld_pad, draft_ld=V + ld_pad, features=seed % 3 == 0)
+    compare_verify(g, target, dmode, toks, cu, k, V, mode, tau, seed, step)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("mode", ["stochastic", "greedy"])
 @pytest.mark.parametrize("which", ["vocab", "drafts"])
