@@ -59,8 +59,8 @@ METRIC = ("verify rows/sec (K+1 rows/req × vocab) + achieved HBM GB/s; "
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="b256_v129280")
     ap.add_argument("--mode", choices=["stochastic", "greedy"], default="stochastic")
     ap.add_argument("--replicas", type=int, default=4)
