@@ -900,6 +900,50 @@ def test_verify_is_deterministic_and_stream_safe():
     assert not np.array_equal(a["tokens"], c["tokens"])
 
 
+def test_concurrent_calls_on_two_streams():
+    """Two different batches verified (and budgeted) at the same time on two
+    streams, each call with its own workspace: every output equals the same
+    call run alone (no state shared between calls outside the arguments)."""
+    import adaptive_draft_verification_amd as sv
+    rng = np.random.default_rng(53)
+    cases = []
+    for n, k, V, dtype in ((24, 5, 30011, torch.bfloat16), (17, 3, 12007, torch.float32)):
+        target, draft, toks, cu = synthetic(rng, n, k, V)
+        conf = rng.uniform(0.2, 1.0, (n, k)).astype(np.float32)
+        dl = rng.integers(0, k + 1, n).astype(np.int32)
+        cost = np.maximum(1.0, np.arange(n + n * k + 1) / 8.0).astype(np.float32)
+        cases.append(dict(t=to_dev(target, dtype), d=to_dev(draft, dtype),
+                          toks=to_dev(np.asarray(toks, np.int32)),
+                          cu=to_dev(np.asarray(cu, np.int32)), conf=to_dev(conf), dl=to_dev(dl),
+                          cost=to_dev(cost), n=n))
+
+    def run(c, stream):
+        v = sv.verify(c["t"], c["d"], c["toks"], c["cu"], sv.SV_STOCHASTIC, 0.9, 3, 8,
+                      stream=stream)
+        b = sv.budget_select(c["conf"], c["dl"], c["cost"], c["n"], c["n"], stream=stream)
+        return v, b
+
+    ref = [run(c, None) for c in cases]
+    torch.cuda.synchronize()
+    ref = [({k: x.cpu() for k, x in v.items()}, {k: x.cpu() for k, x in b.items()})
+           for v, b in ref]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(4):  # enqueued back to back on both streams, no wait in between
+        with torch.cuda.stream(s1):
+            o1 = run(cases[0], s1)
+        with torch.cuda.stream(s2):
+            o2 = run(cases[1], s2)
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    for o1, o2 in outs:
+        for (v, b), (rv, rb) in zip((o1, o2), ref):
+            for key in rv:
+                assert torch.equal(v[key].cpu(), rv[key]), key
+            for key in rb:
+                assert torch.equal(b[key].cpu(), rb[key]), key
+
+
 def test_debug_environment_variables(monkeypatch):
     """SV_DEBUG_CHECKS=1 refuses, on the host and before any launch, index data
     the kernels would flag in dev_error (SV_ERR_DATA; no output touched), and
