@@ -21,7 +21,10 @@ import sys
 import tempfile
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SKIP = ("_work", ".git", "gpurun_out", "__pycache__", "profiles", "*.so")
+# what the CPU tests read (the built library stays out: the tests that need it skip)
+KEEP = ("oracle", "tests", "workloads", "include", "adaptive_draft_verification_amd",
+        "pytest.ini")
+SKIP = ("__pycache__", "*.so")
 PYTEST = ["-m", "pytest", "tests", "-q", "-x", "-m", "not gpu", "-p", "no:cacheprovider",
           "-k", "not chi_square and not uniformity",
           "--ignore=tests/test_gpu_parity.py", "--ignore=tests/test_zz_no_alloc.py",
@@ -110,7 +113,14 @@ def run(entry, scratch):
     d = tempfile.mkdtemp(dir=scratch)
     try:
         dst = os.path.join(d, "repo")
-        shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(*SKIP))
+        os.makedirs(dst)
+        for item in KEEP:
+            src = os.path.join(ROOT, item)
+            if os.path.isdir(src):
+                shutil.copytree(src, os.path.join(dst, item),
+                                ignore=shutil.ignore_patterns(*SKIP))
+            elif os.path.exists(src):
+                shutil.copy2(src, os.path.join(dst, item))
         if old is not None:
             path = os.path.join(dst, "oracle", f)
             text = open(path).read()
