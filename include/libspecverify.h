@@ -341,6 +341,11 @@ sv_status sv_pack_varlen(const int32_t* kept, const int32_t* last_token,
  *                pass 1 accumulates them while it streams the draft rows.
  * A faulty request (any SV_DEV_* bit of its own) writes -1 to all of its
  * outputs.
+ * Numerics: fp32.  Each probability carries a few fp32 ulps of error (the
+ * exp2 instruction, the rounding of its exponent, the normalisations), which
+ * p(d), q(d) and the residual mass inherit; the token at L is the draw above
+ * with its cumulative weights rounded to fp32.  Repeated calls with the same
+ * arguments give bit-identical outputs, on any stream.
  * ws:            sv_verify_workspace_bytes(n_req, k_max) bytes (per-part
  *                row statistics and draft-row feature sums passed from the
  *                first launch to the second).  Calls that overlap in time
