@@ -16,7 +16,7 @@ def build() -> str:
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         raise RuntimeError("no C compiler to build tests/c_gpu_client")
-    cmd = [cc, "-std=gnu11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+    cmd = [cc, "-std=gnu11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
            "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"), SRC,
            "-o", EXE + ".tmp",
            "-L", os.path.join(ROOT, "adaptive_draft_verification_amd"), "-l:libspecverify.so",
