@@ -824,6 +824,8 @@ def main():
         "verify_rows_per_s": round(rows_t / (float(np.median(verify_us)) * 1e-6), 1),
         "verify_gbps": round((pass1_bytes + pass2_bytes)
                              / (float(np.median(verify_us)) * 1e-6) / 1e9, 1),
+        "verify_frac": round((pass1_bytes + pass2_bytes) / (float(np.median(verify_us)) * 1e-6)
+                             / 1e9 / HBM_PEAK_GBPS, 4),
         "gpu_step_us": round(float(np.mean(stage_ms.sum(axis=1))) * 1e3, 2),
         "launch": "hip-graph replay" if graphs else "eager",
         "step_us_p10_p50_p90": step_pct,
