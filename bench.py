@@ -390,6 +390,28 @@ class Leg:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / iters
 
+    def verify_launch_ms(self, iters):
+        """Mean duration of the whole verify call (both passes, no event between
+        them): `iters` calls back to back (replicas in turn) between two events on
+        the launch stream, the same draws as the step's."""
+        sv, torch, w = self.sv, self.torch, self.w
+        reps = self.replicas
+
+        def call(i):
+            tp_, dr_ = reps[i % len(reps)]
+            sv.sv_verify_stages(tp_, dr_, self.toks_d, self.verify_cu, self.mode, w.tau, w.seed,
+                                i, self.tok_out, self.acc_out, self.ws, 3, self.p_out,
+                                self.q_out, self.res_out, self.err, vocab=w.vocab)
+        for i in range(2):
+            call(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(iters):
+            call(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
     def full_k_inputs(self):
         """Every draft kept: request r's rows 0..K_r packed at cu_full[r] (the layout a
         varlen target forward writes), gathered from the per-request stride K+1."""
@@ -638,6 +660,7 @@ def main():
     pass1_ms, pass2_ms = float(np.mean(stage_ms[:, 2])), float(np.mean(stage_ms[:, 3]))
     verify_us = (stage_ms[:, 2] + stage_ms[:, 3]) * 1e3
     roof_ms = leg.pass1_launch_ms(args.steps)
+    verify_ms = leg.verify_launch_ms(args.steps)
     pass1_bytes = leg.pass1_bytes(rows_t, rows_d)
     pass2_bytes = float(np.mean(p2_ids)) * esize
     achieved = pass1_bytes / (roof_ms * 1e-3) / 1e9
@@ -826,6 +849,10 @@ def main():
                              / (float(np.median(verify_us)) * 1e-6) / 1e9, 1),
         "verify_frac": round((pass1_bytes + pass2_bytes) / (float(np.median(verify_us)) * 1e-6)
                              / 1e9 / HBM_PEAK_GBPS, 4),
+        # the same call timed back to back, no event between its two passes
+        "verify_launch_us": round(verify_ms * 1e3, 2),
+        "verify_launch_frac": round((pass1_bytes + pass2_bytes) / (verify_ms * 1e-3) / 1e9
+                                    / HBM_PEAK_GBPS, 4),
         "gpu_step_us": round(float(np.mean(stage_ms.sum(axis=1))) * 1e3, 2),
         "launch": "hip-graph replay" if graphs else "eager",
         "step_us_p10_p50_p90": step_pct,
